@@ -1,0 +1,166 @@
+/*
+ * ra.h -- C ABI of the MI355X (gfx950) ring-attention library (libra.so).
+ *
+ * The library computes the forward pass of exact ring attention for
+ * sequence-parallel ranks that are simulated on one GPU: all P key/value
+ * shards are resident, and each rank's query block visits them in ring
+ * order.  It also computes attention of a few query tokens against a KV cache
+ * split into shards, and merges the per-shard (O, lse) partials.
+ *
+ * Sources (the pages this follows):
+ *   [L8]  Lesson 8 "Context Parallelism (CP)", hpc.payai.win: section 1
+ *         (sequence split, s_local = s / N_cp, tensors (b, s_local, h)),
+ *         section 2 (ring loop: Q_r stays, K/V move r -> r+1, at step t rank r
+ *         holds the block from (r - t) mod P), section 3 (online softmax
+ *         update of (m, l, O)), section 4 (causal mask j <= i; naive split and
+ *         the zig-zag split where rank r holds chunks r and 2P-1-r).
+ *   [P1]  "Paralelismo de sequencia e atencao de anel", aiunderstanding.org:
+ *         every query ends up seeing every key; the result equals full
+ *         attention.
+ *   [HX]  "NVIDIA Helix Parallelism" article, storagereview.com, phase 1: the
+ *         KV cache is split along the sequence across devices, each computes a
+ *         partial result, and one exchange combines them.
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The
+ *     library never allocates, frees or keeps them.  Every call validates its
+ *     arguments, enqueues kernels on `stream` (a hipStream_t passed as void*;
+ *     NULL is the default stream) and returns without synchronising.  A
+ *     kernel fault surfaces at the caller's next synchronisation.
+ *   - Layouts are row-major with the last dimension contiguous.  Sequence
+ *     tensors are [B, S, H, d]; d (head dimension) is 64 or 128.
+ *   - dtype: RA_DTYPE_F32 (float) or RA_DTYPE_BF16 (bfloat16 bit patterns,
+ *     uint16).  Q, K, V and O share the dtype.  LSE and partials are fp32.
+ *   - The softmax scale is 1/sqrt(d) ([L8] section 1).
+ *   - Grouped-query attention: query head h reads key/value head
+ *     h / (Hq/Hkv) (contiguous groups; Hq must be a multiple of Hkv).
+ *   - LSE is the natural-log softmax denominator of the scaled scores,
+ *     m + ln(sum_j exp(s_j - m)); a row that sees no key gets O = 0 and
+ *     LSE = -inf.
+ *   - Return value: RA_OK (0) or a negative ra_status.  Argument checks run
+ *     before any HIP call, so invalid arguments are reported without touching
+ *     the device.  ra_last_error() gives a message for the calling thread's
+ *     last failure.
+ *   - Calls are re-entrant; the only global state is the thread-local error
+ *     message.
+ */
+#ifndef RA_H
+#define RA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    RA_OK = 0,
+    RA_ERR_INVALID_ARG = -1, /* null pointer, size <= 0, rank out of range, bad enum */
+    RA_ERR_UNSUPPORTED = -2, /* valid but not implemented: d, Hq % Hkv, uneven split */
+    RA_ERR_HIP = -3          /* a HIP runtime call or kernel launch failed */
+} ra_status;
+
+typedef enum {
+    RA_LAYOUT_CONTIGUOUS = 0, /* P shards of S/P tokens; shard r = tokens [r*S/P, (r+1)*S/P) */
+    RA_LAYOUT_ZIGZAG = 1      /* 2P chunks of S/(2P) tokens; shard r = [chunk r ; chunk 2P-1-r] */
+} ra_layout;
+
+typedef enum { RA_DTYPE_F32 = 0, RA_DTYPE_BF16 = 1 } ra_dtype;
+
+/*
+ * Rank-sharded sequence order.  A sequence tensor "in sharded order" stores
+ * shard 0's tokens, then shard 1's, ... (each shard S/P tokens).  Under
+ * RA_LAYOUT_CONTIGUOUS this is the natural order.  Under RA_LAYOUT_ZIGZAG
+ * shard r holds chunk r followed by chunk 2P-1-r ([L8] section 4B and the
+ * exercise's answer, which lists the chunks in that order).  The causal mask
+ * always compares natural (global) positions ([L8] section 4).
+ */
+
+/*
+ * ra_fwd_rank -- forward pass of one simulated rank ([L8] sections 2-4).
+ *
+ * Rank `rank` keeps its query block Q_r fixed and, for t = 0..P-1, attends the
+ * resident K/V shard (rank - t) mod P, folding each block into its running
+ * online-softmax state; after P steps it writes O_r and LSE_r.
+ *
+ *   Q_r   [B, S/P, Hq, d]   the rank's local queries (its shard of Q)
+ *   K, V  [B, S, Hkv, d]    all P shards, in sharded order
+ *   O_r   [B, S/P, Hq, d]   output, same dtype as Q
+ *   LSE_r [B, Hq, S/P]      fp32 output
+ *   causal: 0 or 1; layout: ra_layout; dtype: ra_dtype.
+ * Requirements: S % P == 0 (contiguous) or S % (2P) == 0 (zig-zag);
+ * 0 <= rank < P; Hq % Hkv == 0; d in {64, 128}.  Q_r/O_r must not alias K/V.
+ * For B == 1, Q_r/O_r may point at rows rank*S/P of full sharded tensors.
+ * The rows written are bit-identical to the same rows of ra_fwd_all.
+ */
+int ra_fwd_rank(const void* Q_r, const void* K, const void* V, void* O_r, float* LSE_r,
+                int B, int Hq, int Hkv, int64_t S, int d, int P, int rank,
+                int causal, int layout, int dtype, void* stream);
+
+/*
+ * ra_fwd_all -- all P simulated ranks in one launch.
+ *   Q, O [B, S, Hq, d], K, V [B, S, Hkv, d], LSE [B, Hq, S]; all sequence
+ *   dimensions in sharded order.  Same requirements as ra_fwd_rank.
+ * Equals the concatenation of ra_fwd_rank over rank = 0..P-1, bit for bit.
+ */
+int ra_fwd_all(const void* Q, const void* K, const void* V, void* O, float* LSE,
+               int B, int Hq, int Hkv, int64_t S, int d, int P,
+               int causal, int layout, int dtype, void* stream);
+
+/*
+ * ra_merge_partials -- combine (O, lse) partials that were computed over
+ * disjoint key sets of the same query rows ([L8] section 3 applied to whole
+ * shards; [HX] phase 1):
+ *   M = max_p lse_p, w_p = exp(lse_p - M),
+ *   lse = M + ln(sum_p w_p), O = sum_p w_p O_p / sum_p w_p.
+ * Partials with lse_p = -inf carry weight 0; a row whose partials are all
+ * -inf gets O = 0, lse = -inf.
+ *   O_parts   [n_parts, rows, d] fp32     lse_parts [n_parts, rows] fp32
+ *   O         [rows, d] in out_dtype      lse       [rows] fp32 (may be NULL)
+ * Requirements: n_parts >= 1, rows >= 1, d in {64, 128}.
+ */
+int ra_merge_partials(const float* O_parts, const float* lse_parts, void* O, float* lse,
+                      int n_parts, int64_t rows, int d, int out_dtype, void* stream);
+
+/*
+ * ra_attn_partial -- per-shard partial attention over a KV cache that is
+ * split along the sequence ([HX] phase 1).  Non-causal: every query sees
+ * every key of its shard.
+ *   Q  [B, Sq, Hq, d]      K, V [B, Skv, Hkv, d]   (dtype)
+ *   Skv is cut into n_parts contiguous parts of ceil(Skv / n_parts) keys
+ *   (the last part may be shorter or empty); part p covers keys
+ *   [p*ceil, min(Skv, (p+1)*ceil)).
+ *   O_parts   [n_parts, B*Sq*Hq, d] fp32, row (b*Sq + i)*Hq + h
+ *   lse_parts [n_parts, B*Sq*Hq]    fp32
+ * Requirements: Sq * (Hq/Hkv) <= 32, n_parts >= 1, d in {64, 128}.
+ * An empty part yields O = 0, lse = -inf, which ra_merge_partials ignores.
+ */
+int ra_attn_partial(const void* Q, const void* K, const void* V, float* O_parts,
+                    float* lse_parts, int B, int Hq, int Hkv, int64_t Sq, int64_t Skv,
+                    int d, int n_parts, int dtype, void* stream);
+
+/*
+ * ra_layout_gather -- move a sequence tensor between natural order and
+ * sharded order ([L8] section 4B: the zig-zag chunk map).
+ *   src, dst  [outer, S, inner_bytes] viewed as bytes; must not overlap.
+ *   inverse = 0: natural -> sharded; inverse = 1: sharded -> natural.
+ *   layout RA_LAYOUT_CONTIGUOUS is the identity (a copy).
+ * Use outer = B and inner_bytes = H*d*elem for Q/K/V/O, and outer = B*Hq,
+ * inner_bytes = 4 for an LSE array [B, Hq, S].
+ * Requirements: S % (2P) == 0 for zig-zag, inner_bytes >= 1.
+ */
+int ra_layout_gather(const void* src, void* dst, int64_t outer, int64_t S,
+                     int64_t inner_bytes, int P, int layout, int inverse, void* stream);
+
+/* Message describing the calling thread's last non-OK status ("" if none). */
+const char* ra_last_error(void);
+
+/* Library version string. */
+const char* ra_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RA_H */

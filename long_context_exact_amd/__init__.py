@@ -1,0 +1,185 @@
+"""MI355X-native exact ring attention (gfx950 HIP kernels behind a C ABI).
+
+This package is a thin binding over ``libra.so`` (see ``include/ra.h``):
+the functions below only check tensor shapes and dtypes, take raw device
+pointers and the current HIP stream from PyTorch, and call the C entry point
+of the same name.  All arithmetic runs in the library's kernels; there is no
+fallback.  If the library is missing the first call raises.
+
+Tensors are [B, S, H, d] with d contiguous; sequence dimensions are in the
+rank-sharded order described in ``include/ra.h``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libra.so")
+
+RA_OK, RA_ERR_INVALID_ARG, RA_ERR_UNSUPPORTED, RA_ERR_HIP = 0, -1, -2, -3
+LAYOUTS = {"contiguous": 0, "zigzag": 1}
+DTYPE_F32, DTYPE_BF16 = 0, 1
+
+EXPORTS = ("ra_fwd_rank", "ra_fwd_all", "ra_merge_partials", "ra_attn_partial",
+           "ra_layout_gather", "ra_last_error", "ra_version")
+
+_lib = None
+
+
+class RaError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"libra status {code}: {msg}")
+        self.code = code
+
+
+def lib() -> ctypes.CDLL:
+    """Load libra.so (built in-tree by ``long_context_exact_amd.build``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m long_context_exact_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, fp = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_void_p
+        L.ra_fwd_rank.argtypes = [vp, vp, vp, vp, fp, i32, i32, i32, i64, i32, i32, i32, i32, i32,
+                                  i32, vp]
+        L.ra_fwd_all.argtypes = [vp, vp, vp, vp, fp, i32, i32, i32, i64, i32, i32, i32, i32, i32, vp]
+        L.ra_merge_partials.argtypes = [fp, fp, vp, fp, i32, i64, i32, i32, vp]
+        L.ra_attn_partial.argtypes = [vp, vp, vp, fp, fp, i32, i32, i32, i64, i64, i32, i32, i32, vp]
+        L.ra_layout_gather.argtypes = [vp, vp, i64, i64, i64, i32, i32, i32, vp]
+        for f in ("ra_fwd_rank", "ra_fwd_all", "ra_merge_partials", "ra_attn_partial",
+                  "ra_layout_gather"):
+            getattr(L, f).restype = ctypes.c_int
+        L.ra_last_error.restype = ctypes.c_char_p
+        L.ra_version.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def last_error() -> str:
+    return lib().ra_last_error().decode()
+
+
+def _check(rc: int) -> None:
+    if rc != RA_OK:
+        raise RaError(rc, last_error())
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream):
+    if stream is not None:
+        return ctypes.c_void_p(int(stream))
+    return ctypes.c_void_p(_torch().cuda.current_stream().cuda_stream)
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    if t.dtype == torch.float32:
+        return DTYPE_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _dev(t, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _layout(layout) -> int:
+    return LAYOUTS[layout] if isinstance(layout, str) else int(layout)
+
+
+def ra_fwd_rank(Q_r, K, V, O_r, LSE_r, P: int, rank: int, causal: bool, layout, stream=None):
+    """One simulated rank: Q_r/O_r [B, S/P, Hq, d], K/V [B, S, Hkv, d] (all P
+    shards, sharded order), LSE_r [B, Hq, S/P] float32."""
+    B, S, Hkv, d = K.shape
+    Hq = Q_r.shape[2]
+    if tuple(Q_r.shape) != (B, S // P, Hq, d) or O_r.shape != Q_r.shape or V.shape != K.shape:
+        raise ValueError("shape mismatch")
+    if tuple(LSE_r.shape) != (B, Hq, S // P) or LSE_r.dtype != _torch().float32:
+        raise ValueError("LSE_r must be float32 [B, Hq, S/P]")
+    dt = _dtype_code(Q_r)
+    if not (K.dtype == V.dtype == O_r.dtype == Q_r.dtype):
+        raise TypeError("Q, K, V, O must share a dtype")
+    _check(lib().ra_fwd_rank(_dev(Q_r, "Q_r"), _dev(K, "K"), _dev(V, "V"), _dev(O_r, "O_r"),
+                             _dev(LSE_r, "LSE_r"), B, Hq, Hkv, S, d, P, rank, int(bool(causal)),
+                             _layout(layout), dt, _stream(stream)))
+
+
+def ra_fwd_all(Q, K, V, O, LSE, P: int, causal: bool, layout, stream=None):
+    """All P simulated ranks: Q/O [B, S, Hq, d], K/V [B, S, Hkv, d],
+    LSE [B, Hq, S] float32, sharded order."""
+    B, S, Hkv, d = K.shape
+    Hq = Q.shape[2]
+    if tuple(Q.shape) != (B, S, Hq, d) or O.shape != Q.shape or V.shape != K.shape:
+        raise ValueError("shape mismatch")
+    if tuple(LSE.shape) != (B, Hq, S) or LSE.dtype != _torch().float32:
+        raise ValueError("LSE must be float32 [B, Hq, S]")
+    dt = _dtype_code(Q)
+    if not (K.dtype == V.dtype == O.dtype == Q.dtype):
+        raise TypeError("Q, K, V, O must share a dtype")
+    _check(lib().ra_fwd_all(_dev(Q, "Q"), _dev(K, "K"), _dev(V, "V"), _dev(O, "O"),
+                            _dev(LSE, "LSE"), B, Hq, Hkv, S, d, P, int(bool(causal)),
+                            _layout(layout), dt, _stream(stream)))
+
+
+def ra_merge_partials(O_parts, lse_parts, O, lse=None, stream=None):
+    """O_parts [n_parts, rows, d] fp32, lse_parts [n_parts, rows] fp32 ->
+    O [rows, d] (bf16 or fp32), lse [rows] fp32 (optional)."""
+    n_parts, rows, d = O_parts.shape
+    torch = _torch()
+    if O_parts.dtype != torch.float32 or lse_parts.dtype != torch.float32:
+        raise TypeError("partials must be float32")
+    if tuple(lse_parts.shape) != (n_parts, rows) or O.numel() != rows * d:
+        raise ValueError("shape mismatch")
+    lse_ptr = ctypes.c_void_p(0)
+    if lse is not None:
+        if lse.numel() != rows or lse.dtype != torch.float32:
+            raise ValueError("lse must be float32 [rows]")
+        lse_ptr = _dev(lse, "lse")
+    _check(lib().ra_merge_partials(_dev(O_parts, "O_parts"), _dev(lse_parts, "lse_parts"),
+                                   _dev(O, "O"), lse_ptr, n_parts, rows, d, _dtype_code(O),
+                                   _stream(stream)))
+
+
+def ra_attn_partial(Q, K, V, O_parts, lse_parts, n_parts: int, stream=None):
+    """Q [B, Sq, Hq, d], K/V [B, Skv, Hkv, d] -> O_parts [n_parts, B*Sq*Hq, d]
+    and lse_parts [n_parts, B*Sq*Hq] (fp32), keys cut into n_parts parts."""
+    B, Sq, Hq, d = Q.shape
+    _, Skv, Hkv, _ = K.shape
+    rows = B * Sq * Hq
+    if tuple(O_parts.shape) != (n_parts, rows, d) or tuple(lse_parts.shape) != (n_parts, rows):
+        raise ValueError("partials shape mismatch")
+    if not (K.dtype == V.dtype == Q.dtype):
+        raise TypeError("Q, K, V must share a dtype")
+    _check(lib().ra_attn_partial(_dev(Q, "Q"), _dev(K, "K"), _dev(V, "V"),
+                                 _dev(O_parts, "O_parts"), _dev(lse_parts, "lse_parts"), B, Hq, Hkv,
+                                 Sq, Skv, d, n_parts, _dtype_code(Q), _stream(stream)))
+
+
+def ra_layout_gather(src, dst, S: int, P: int, layout, inverse: bool, outer: int | None = None,
+                     stream=None):
+    """Natural <-> sharded order of a tensor viewed as [outer, S, inner]."""
+    if src.shape != dst.shape or src.dtype != dst.dtype:
+        raise ValueError("src and dst must match")
+    nbytes = src.numel() * src.element_size()
+    if outer is None:
+        outer = src.shape[0]
+    inner = nbytes // (outer * S)
+    if outer * S * inner != nbytes:
+        raise ValueError("tensor does not view as [outer, S, inner]")
+    _check(lib().ra_layout_gather(_dev(src, "src"), _dev(dst, "dst"), outer, S, inner, P,
+                                  _layout(layout), int(bool(inverse)), _stream(stream)))
+
+
+def version() -> str:
+    return lib().ra_version().decode()

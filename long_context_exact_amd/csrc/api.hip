@@ -1,0 +1,204 @@
+// api.hip -- the extern "C" entry points of libra.so (declared in ra.h):
+// argument validation, launch planning and kernel dispatch.  Validation
+// happens before any HIP call, so bad arguments are reported without a device.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "../../include/ra.h"
+#include "ra_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int ok() {
+    g_err[0] = '\0';
+    return RA_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(RA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+// Checks shared by ra_fwd_rank and ra_fwd_all.
+int check_fwd(const void* Q, const void* K, const void* V, const void* O, const float* LSE, int B,
+              int Hq, int Hkv, int64_t S, int d, int P, int causal, int layout, int dtype) {
+    if (!Q || !K || !V || !O || !LSE) return fail(RA_ERR_INVALID_ARG, "null tensor pointer");
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || S <= 0 || P <= 0)
+        return fail(RA_ERR_INVALID_ARG, "sizes must be positive (B=%d Hq=%d Hkv=%d S=%lld P=%d)", B,
+                    Hq, Hkv, (long long)S, P);
+    if (causal != 0 && causal != 1) return fail(RA_ERR_INVALID_ARG, "causal must be 0 or 1");
+    if (layout != RA_LAYOUT_CONTIGUOUS && layout != RA_LAYOUT_ZIGZAG)
+        return fail(RA_ERR_INVALID_ARG, "unknown layout %d", layout);
+    if (dtype != RA_DTYPE_F32 && dtype != RA_DTYPE_BF16)
+        return fail(RA_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+    if (d != 64 && d != 128) return fail(RA_ERR_UNSUPPORTED, "head dim %d (supported: 64, 128)", d);
+    if (Hq % Hkv != 0) return fail(RA_ERR_UNSUPPORTED, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+    if (layout == RA_LAYOUT_CONTIGUOUS && S % P != 0)
+        return fail(RA_ERR_UNSUPPORTED, "S=%lld does not split into P=%d equal shards", (long long)S, P);
+    if (layout == RA_LAYOUT_ZIGZAG && S % (2 * (int64_t)P) != 0)
+        return fail(RA_ERR_UNSUPPORTED, "S=%lld does not split into 2P=%d equal chunks", (long long)S,
+                    2 * P);
+    if (P > 4096) return fail(RA_ERR_UNSUPPORTED, "P=%d exceeds 4096", P);
+    return RA_OK;
+}
+
+ra::FwdParams plan_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int B,
+                       int Hq, int Hkv, int64_t S, int d, int P, int causal, int layout, int dtype,
+                       int rank_lo, int n_ranks, int q_local) {
+    ra::FwdParams p;
+    p.Q = Q;
+    p.K = K;
+    p.V = V;
+    p.O = O;
+    p.LSE = LSE;
+    p.S = S;
+    p.n = S / P;
+    p.zigzag = layout == RA_LAYOUT_ZIGZAG;
+    p.c = p.zigzag ? p.n / 2 : p.n;
+    p.q_rows = q_local ? p.n : S;
+    p.B = B;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.G = Hq / Hkv;
+    p.P = P;
+    p.causal = causal;
+    p.rank_lo = rank_lo;
+    p.n_ranks = n_ranks;
+    p.q_local = q_local;
+    const int bm = dtype == RA_DTYPE_BF16 ? ra::FWD_BF16_BLOCK_M : ra::FWD_F32_BLOCK_M;
+    p.tiles_per_chunk = (int)((p.c + bm - 1) / bm);
+    p.chunks_per_rank = p.zigzag ? 2 : 1;
+    const int pairs = B * Hkv;
+    p.xcd_pairs = (pairs % 8 == 0) ? pairs / 8 : 0;
+    p.scale = (float)(1.0 / sqrt((double)d));
+    p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d));
+    return p;
+}
+
+int launch_fwd(const ra::FwdParams& p, int d, int dtype, void* stream) {
+    const int64_t tiles = (int64_t)p.n_ranks * p.chunks_per_rank * p.tiles_per_chunk;
+    const int64_t grid = tiles * p.B * p.Hq;
+    if (grid > 0x7fffffffLL) return fail(RA_ERR_UNSUPPORTED, "grid of %lld work-groups", (long long)grid);
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = dtype == RA_DTYPE_BF16 ? ra::launch_fwd_bf16(p, d, s) : ra::launch_fwd_f32(p, d, s);
+    return hip_status(e, "attention kernel launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int ra_fwd_rank(const void* Q_r, const void* K, const void* V, void* O_r, float* LSE_r, int B,
+                int Hq, int Hkv, int64_t S, int d, int P, int rank, int causal, int layout, int dtype,
+                void* stream) {
+    int rc = check_fwd(Q_r, K, V, O_r, LSE_r, B, Hq, Hkv, S, d, P, causal, layout, dtype);
+    if (rc != RA_OK) return rc;
+    if (rank < 0 || rank >= P) return fail(RA_ERR_INVALID_ARG, "rank %d outside [0, %d)", rank, P);
+    ra::FwdParams p = plan_fwd(Q_r, K, V, O_r, LSE_r, B, Hq, Hkv, S, d, P, causal, layout, dtype,
+                               rank, 1, 1);
+    return launch_fwd(p, d, dtype, stream);
+}
+
+int ra_fwd_all(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int Hq,
+               int Hkv, int64_t S, int d, int P, int causal, int layout, int dtype, void* stream) {
+    int rc = check_fwd(Q, K, V, O, LSE, B, Hq, Hkv, S, d, P, causal, layout, dtype);
+    if (rc != RA_OK) return rc;
+    ra::FwdParams p = plan_fwd(Q, K, V, O, LSE, B, Hq, Hkv, S, d, P, causal, layout, dtype, 0, P, 0);
+    return launch_fwd(p, d, dtype, stream);
+}
+
+int ra_merge_partials(const float* O_parts, const float* lse_parts, void* O, float* lse,
+                      int n_parts, int64_t rows, int d, int out_dtype, void* stream) {
+    if (!O_parts || !lse_parts || !O) return fail(RA_ERR_INVALID_ARG, "null tensor pointer");
+    if (n_parts <= 0 || rows <= 0)
+        return fail(RA_ERR_INVALID_ARG, "n_parts=%d rows=%lld must be positive", n_parts,
+                    (long long)rows);
+    if (out_dtype != RA_DTYPE_F32 && out_dtype != RA_DTYPE_BF16)
+        return fail(RA_ERR_INVALID_ARG, "unknown dtype %d", out_dtype);
+    if (d != 64 && d != 128) return fail(RA_ERR_UNSUPPORTED, "head dim %d (supported: 64, 128)", d);
+    if ((rows + 3) / 4 > 0x7fffffffLL) return fail(RA_ERR_UNSUPPORTED, "too many rows");
+    ra::MergeParams p;
+    p.O_parts = O_parts;
+    p.lse_parts = lse_parts;
+    p.O = O;
+    p.lse = lse;
+    p.rows = rows;
+    p.n_parts = n_parts;
+    p.out_bf16 = out_dtype == RA_DTYPE_BF16;
+    return hip_status(ra::launch_merge(p, d, (hipStream_t)stream), "merge kernel launch");
+}
+
+int ra_attn_partial(const void* Q, const void* K, const void* V, float* O_parts, float* lse_parts,
+                    int B, int Hq, int Hkv, int64_t Sq, int64_t Skv, int d, int n_parts, int dtype,
+                    void* stream) {
+    if (!Q || !K || !V || !O_parts || !lse_parts) return fail(RA_ERR_INVALID_ARG, "null tensor pointer");
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || Sq <= 0 || Skv <= 0 || n_parts <= 0)
+        return fail(RA_ERR_INVALID_ARG, "sizes must be positive");
+    if (dtype != RA_DTYPE_F32 && dtype != RA_DTYPE_BF16)
+        return fail(RA_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+    if (d != 64 && d != 128) return fail(RA_ERR_UNSUPPORTED, "head dim %d (supported: 64, 128)", d);
+    if (Hq % Hkv != 0) return fail(RA_ERR_UNSUPPORTED, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+    if (Sq * (Hq / Hkv) > 32)
+        return fail(RA_ERR_UNSUPPORTED, "Sq*(Hq/Hkv)=%lld exceeds 32 query rows per kv head",
+                    (long long)(Sq * (Hq / Hkv)));
+    const int64_t grid = (int64_t)B * Hkv * n_parts;
+    if (grid > 0x7fffffffLL) return fail(RA_ERR_UNSUPPORTED, "grid of %lld work-groups", (long long)grid);
+    ra::DecodeParams p;
+    p.Q = Q;
+    p.K = K;
+    p.V = V;
+    p.O_parts = O_parts;
+    p.lse_parts = lse_parts;
+    p.Sq = Sq;
+    p.Skv = Skv;
+    p.part_len = (Skv + n_parts - 1) / n_parts;
+    p.B = B;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.G = Hq / Hkv;
+    p.n_parts = n_parts;
+    p.splits = 1;
+    p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d));
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = dtype == RA_DTYPE_BF16 ? ra::launch_decode_bf16(p, d, s) : ra::launch_decode_f32(p, d, s);
+    return hip_status(e, "decode kernel launch");
+}
+
+int ra_layout_gather(const void* src, void* dst, int64_t outer, int64_t S, int64_t inner_bytes, int P,
+                     int layout, int inverse, void* stream) {
+    if (!src || !dst) return fail(RA_ERR_INVALID_ARG, "null tensor pointer");
+    if (outer <= 0 || S <= 0 || inner_bytes <= 0 || P <= 0)
+        return fail(RA_ERR_INVALID_ARG, "sizes must be positive");
+    if (layout != RA_LAYOUT_CONTIGUOUS && layout != RA_LAYOUT_ZIGZAG)
+        return fail(RA_ERR_INVALID_ARG, "unknown layout %d", layout);
+    if (inverse != 0 && inverse != 1) return fail(RA_ERR_INVALID_ARG, "inverse must be 0 or 1");
+    if (layout == RA_LAYOUT_ZIGZAG && S % (2 * (int64_t)P) != 0)
+        return fail(RA_ERR_UNSUPPORTED, "S=%lld does not split into 2P=%d equal chunks", (long long)S,
+                    2 * P);
+    if (layout == RA_LAYOUT_CONTIGUOUS && S % P != 0)
+        return fail(RA_ERR_UNSUPPORTED, "S=%lld does not split into P=%d equal shards", (long long)S, P);
+    const uint8_t* s0 = (const uint8_t*)src;
+    const uint8_t* d0 = (const uint8_t*)dst;
+    const int64_t bytes = outer * S * inner_bytes;
+    if (s0 < d0 + bytes && d0 < s0 + bytes) return fail(RA_ERR_INVALID_ARG, "src and dst overlap");
+    return hip_status(ra::launch_layout(src, dst, outer, S, inner_bytes, P,
+                                        layout == RA_LAYOUT_ZIGZAG, inverse, (hipStream_t)stream),
+                      "layout kernel launch");
+}
+
+const char* ra_last_error(void) { return g_err; }
+
+const char* ra_version(void) { return "libra 0.1 (gfx950)"; }
+
+}  // extern "C"

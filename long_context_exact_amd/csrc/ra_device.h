@@ -1,0 +1,155 @@
+// ra_device.h -- device-side helpers shared by the gfx950 kernels of libra.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ra_internal.h"
+
+namespace ra {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLn2 = 0.693147180559945309f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float xor32_max(float x) { return fmaxf(x, __shfl_xor(x, 32, 64)); }
+__device__ __forceinline__ float xor32_sum(float x) { return x + __shfl_xor(x, 32, 64); }
+
+// ----------------------------------------------------------------------------
+// Query tiles of one prefill launch.
+//
+// Work-group id -> (batch, query head, rank, local chunk, tile).  Tiles are
+// handed out heaviest first: under the causal mask the work of a query tile
+// grows with its global position, so tiles are enumerated by descending global
+// chunk and, inside a chunk, descending offset.  When the number of
+// (batch, kv head) pairs is a multiple of the 8 XCDs, work-group ids are
+// grouped so that all query heads reading one kv head run on one XCD (ids are
+// dispatched round-robin over the XCDs) and share its L2.
+// ----------------------------------------------------------------------------
+struct QTile {
+    int b, qh, kvh, rank;
+    int64_t gchunk;  // global chunk id of the tile
+    int64_t q_row0;  // first row in the Q/O tensors
+    int64_t pos0;    // global position of the first row
+    int rows;        // valid rows (<= BLOCK_M)
+};
+
+__device__ __forceinline__ int64_t global_chunk(const FwdParams& p, int rank, int lc) {
+    return lc == 0 ? (int64_t)rank : (int64_t)(2 * p.P - 1 - rank);
+}
+
+template <int BM>
+__device__ __forceinline__ QTile decode_qtile(const FwdParams& p, unsigned id) {
+    QTile t;
+    int trank, pair, g;
+    if (p.xcd_pairs > 0) {
+        const unsigned xcd = id & 7u, k = id >> 3;
+        const unsigned per = (unsigned)(p.xcd_pairs * p.G);
+        trank = (int)(k / per);
+        const unsigned rem = k % per;
+        pair = (int)xcd * p.xcd_pairs + (int)(rem / p.G);
+        g = (int)(rem % p.G);
+    } else {
+        const unsigned per = (unsigned)(p.B * p.Hq);
+        trank = (int)(id / per);
+        const unsigned rem = id % per;
+        pair = (int)(rem / p.G);
+        g = (int)(rem % p.G);
+    }
+    t.b = pair / p.Hkv;
+    t.kvh = pair % p.Hkv;
+    t.qh = t.kvh * p.G + g;
+    const int tpc = p.tiles_per_chunk;
+    const int cidx = trank / tpc;
+    const int j = tpc - 1 - (trank % tpc);
+    int rank, lc;
+    if (!p.zigzag) {
+        rank = p.rank_lo + p.n_ranks - 1 - cidx;
+        lc = 0;
+    } else if (p.n_ranks == 1) {
+        rank = p.rank_lo;
+        lc = cidx == 0 ? 1 : 0;
+    } else {
+        const int gch = 2 * p.P - 1 - cidx;
+        rank = gch < p.P ? gch : 2 * p.P - 1 - gch;
+        lc = gch < p.P ? 0 : 1;
+    }
+    t.rank = rank;
+    t.gchunk = p.zigzag ? global_chunk(p, rank, lc) : (int64_t)rank;
+    const int64_t off = (int64_t)j * BM;
+    t.q_row0 = (p.q_local ? 0 : (int64_t)rank * p.n) + (int64_t)lc * p.c + off;
+    t.pos0 = t.gchunk * p.c + off;
+    const int64_t left = p.c - off;
+    t.rows = left < BM ? (int)left : BM;
+    return t;
+}
+
+// ----------------------------------------------------------------------------
+// Ring visiting order of the key tiles of one query tile.
+//
+// Step t = 0..P-1 visits shard s = (rank - t) mod P (lesson 8, section 2: K/V
+// travel r -> r+1, so after t hops rank r holds the block that started at
+// r - t).  Inside a shard the chunks are visited in local order and each
+// chunk's key tiles in ascending order.  Under the causal mask only the
+// prefix of a chunk whose positions do not exceed the tile's last query is
+// visited; tiles wholly in the future of every query of the tile are skipped.
+// All fields are uniform across the work-group.
+// ----------------------------------------------------------------------------
+struct KvIter {
+    int t, lc, tile, ntiles;
+    int64_t krow;  // first K/V row (sharded order) of the current chunk
+    int64_t kpos;  // global position of that row
+};
+
+__device__ __forceinline__ void kv_seg(const FwdParams& p, int rank, int64_t qmax, int bn,
+                                       KvIter& it) {
+    int s = rank - it.t;
+    if (s < 0) s += p.P;
+    const int64_t gch = p.zigzag ? global_chunk(p, s, it.lc) : (int64_t)s;
+    it.krow = (int64_t)s * p.n + (int64_t)it.lc * p.c;
+    it.kpos = gch * p.c;
+    int64_t vis = p.c;
+    if (p.causal) {
+        vis = qmax - it.kpos + 1;
+        if (vis < 0) vis = 0;
+        if (vis > p.c) vis = p.c;
+    }
+    it.ntiles = (int)((vis + bn - 1) / bn);
+}
+
+__device__ __forceinline__ bool kv_first(const FwdParams& p, int rank, int64_t qmax, int bn,
+                                         KvIter& it) {
+    it.t = 0;
+    it.lc = 0;
+    it.tile = 0;
+    kv_seg(p, rank, qmax, bn, it);
+    while (it.tile >= it.ntiles) {
+        if (++it.lc == p.chunks_per_rank) {
+            it.lc = 0;
+            if (++it.t == p.P) return false;
+        }
+        kv_seg(p, rank, qmax, bn, it);
+    }
+    return true;
+}
+
+__device__ __forceinline__ bool kv_next(const FwdParams& p, int rank, int64_t qmax, int bn,
+                                        KvIter& it) {
+    ++it.tile;
+    while (it.tile >= it.ntiles) {
+        if (++it.lc == p.chunks_per_rank) {
+            it.lc = 0;
+            if (++it.t == p.P) return false;
+        }
+        it.tile = 0;
+        kv_seg(p, rank, qmax, bn, it);
+    }
+    return true;
+}
+
+}  // namespace ra

@@ -1,0 +1,77 @@
+// ra_internal.h -- parameter blocks shared by the host entry points and the
+// kernel launchers of libra.so.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ra {
+
+// Which query tiles one prefill launch covers and how they are ordered.
+//
+// The queries of a rank are cut into tiles that never straddle a chunk (a
+// rank owns one chunk under the contiguous split and two under zig-zag), so
+// the global positions inside one query tile are consecutive.  Key tiles
+// likewise stay inside one chunk.
+struct FwdParams {
+    const void* Q;     // [B, q_rows, Hq, d]
+    const void* K;     // [B, S, Hkv, d], sharded order
+    const void* V;     // [B, S, Hkv, d], sharded order
+    void* O;           // [B, q_rows, Hq, d]
+    float* LSE;        // [B, Hq, q_rows]
+    int64_t S;         // total tokens (all shards)
+    int64_t n;         // tokens per shard, S / P
+    int64_t c;         // tokens per chunk: n (contiguous) or n / 2 (zig-zag)
+    int64_t q_rows;    // rows of Q/O/LSE: S for all ranks, n for one rank
+    int B, Hq, Hkv, G; // G = Hq / Hkv
+    int P;
+    int zigzag;        // 0 contiguous, 1 zig-zag
+    int causal;
+    int rank_lo;       // first rank of this launch
+    int n_ranks;       // ranks in this launch (P for all, 1 for one rank)
+    int q_local;       // 1: Q/O/LSE rows are rank-local (row 0 = first row of rank_lo)
+    int tiles_per_chunk;   // ceil(c / BLOCK_M)
+    int chunks_per_rank;   // 1 or 2
+    int xcd_pairs;     // (b, kv head) pairs per XCD group, 0 = no XCD grouping
+    float scale_log2;  // log2(e) / sqrt(d)
+    float scale;       // 1 / sqrt(d)
+};
+
+struct DecodeParams {
+    const void* Q;     // [B, Sq, Hq, d]
+    const void* K;     // [B, Skv, Hkv, d]
+    const void* V;
+    float* O_parts;    // [n_parts, B*Sq*Hq, d]
+    float* lse_parts;  // [n_parts, B*Sq*Hq]
+    int64_t Sq, Skv;
+    int64_t part_len;  // ceil(Skv / n_parts)
+    int B, Hq, Hkv, G;
+    int n_parts;
+    int splits;        // work-groups per part
+    float scale_log2;
+};
+
+struct MergeParams {
+    const float* O_parts;
+    const float* lse_parts;
+    void* O;
+    float* lse;
+    int64_t rows;
+    int n_parts;
+    int out_bf16;
+};
+
+// Launchers (each returns hipSuccess or the launch error).
+hipError_t launch_fwd_bf16(const FwdParams& p, int d, hipStream_t s);
+hipError_t launch_fwd_f32(const FwdParams& p, int d, hipStream_t s);
+hipError_t launch_decode_bf16(const DecodeParams& p, int d, hipStream_t s);
+hipError_t launch_decode_f32(const DecodeParams& p, int d, hipStream_t s);
+hipError_t launch_merge(const MergeParams& p, int d, hipStream_t s);
+hipError_t launch_layout(const void* src, void* dst, int64_t outer, int64_t S, int64_t inner_bytes,
+                         int P, int zigzag, int inverse, hipStream_t s);
+
+// Tile shapes of the prefill kernels (the host needs them for the grid).
+constexpr int FWD_BF16_BLOCK_M = 128;
+constexpr int FWD_F32_BLOCK_M = 64;
+
+}  // namespace ra

@@ -1,0 +1,96 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry
+point ra.h declares, and rejects invalid arguments with the documented status
+codes before touching the device."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import long_context_exact_amd as ra
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ra.h")
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+NULL = ctypes.c_void_p(0)
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ra_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_names():
+    assert declared_symbols() == sorted(ra.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = ra.lib()
+    for name in declared_symbols():
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", ra.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r" T (ra_[a-z_]+)$", out, flags=re.M))
+    assert set(declared_symbols()) <= exported
+
+
+def test_version():
+    assert "gfx950" in ra.version()
+
+
+def _fwd_rank(**kw):
+    a = dict(Q=FAKE, K=FAKE, V=FAKE, O=FAKE, L=FAKE, B=1, Hq=8, Hkv=8, S=8192, d=128, P=8,
+             rank=0, causal=1, layout=1, dtype=1)
+    a.update(kw)
+    return ra.lib().ra_fwd_rank(a["Q"], a["K"], a["V"], a["O"], a["L"], a["B"], a["Hq"], a["Hkv"],
+                                a["S"], a["d"], a["P"], a["rank"], a["causal"], a["layout"],
+                                a["dtype"], NULL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Q=NULL), ra.RA_ERR_INVALID_ARG),
+    (dict(L=NULL), ra.RA_ERR_INVALID_ARG),
+    (dict(B=0), ra.RA_ERR_INVALID_ARG),
+    (dict(S=-8), ra.RA_ERR_INVALID_ARG),
+    (dict(rank=8), ra.RA_ERR_INVALID_ARG),
+    (dict(rank=-1), ra.RA_ERR_INVALID_ARG),
+    (dict(causal=2), ra.RA_ERR_INVALID_ARG),
+    (dict(layout=7), ra.RA_ERR_INVALID_ARG),
+    (dict(dtype=5), ra.RA_ERR_INVALID_ARG),
+    (dict(d=96), ra.RA_ERR_UNSUPPORTED),
+    (dict(Hq=12, Hkv=8), ra.RA_ERR_UNSUPPORTED),
+    (dict(S=8200), ra.RA_ERR_UNSUPPORTED),                 # 8200 % 16 != 0 under zig-zag
+    (dict(S=8200, layout=0), ra.RA_ERR_UNSUPPORTED),       # 8200 % 8 == 0 but zig-zag needs 2P
+])
+def test_fwd_rank_rejects(kw, code):
+    if kw == dict(S=8200, layout=0):
+        kw = dict(S=8201, layout=0)
+    assert _fwd_rank(**kw) == code
+    assert ra.last_error() != ""
+
+
+def test_fwd_all_and_others_reject():
+    L = ra.lib()
+    assert L.ra_fwd_all(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 4, 4, 1000, 64, 3, 0, 0, 0, NULL) \
+        == ra.RA_ERR_UNSUPPORTED
+    assert "equal shards" in ra.last_error()
+    assert L.ra_merge_partials(FAKE, FAKE, FAKE, NULL, 0, 10, 128, 1, NULL) == ra.RA_ERR_INVALID_ARG
+    assert L.ra_merge_partials(FAKE, FAKE, FAKE, NULL, 2, 10, 80, 1, NULL) == ra.RA_ERR_UNSUPPORTED
+    assert L.ra_merge_partials(NULL, FAKE, FAKE, NULL, 2, 10, 128, 1, NULL) == ra.RA_ERR_INVALID_ARG
+    # 64 query rows per kv head exceed the 32 MFMA columns of the decode kernel
+    assert L.ra_attn_partial(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 64, 1, 1, 100, 128, 4, 1, NULL) \
+        == ra.RA_ERR_UNSUPPORTED
+    assert L.ra_attn_partial(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 1, 1, 0, 128, 4, 1, NULL) \
+        == ra.RA_ERR_INVALID_ARG
+    assert L.ra_layout_gather(FAKE, FAKE, 1, 30, 16, 4, 1, 0, NULL) == ra.RA_ERR_UNSUPPORTED
+    assert L.ra_layout_gather(FAKE, FAKE, 1, 32, 16, 4, 1, 0, NULL) == ra.RA_ERR_INVALID_ARG  # overlap
+    assert L.ra_layout_gather(FAKE, FAKE, 1, 32, 16, 4, 1, 3, NULL) == ra.RA_ERR_INVALID_ARG
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(ra, "_lib", None)
+    monkeypatch.setattr(ra, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        ra.lib()

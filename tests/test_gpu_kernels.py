@@ -1,0 +1,202 @@
+"""GPU parity of the three kernels against the fp64 oracle on small shapes
+that span several tiles and ragged tails, in every layout / mask / dtype /
+head-dim combination, plus the structural checks: ra_fwd_all equals the
+concatenated ra_fwd_rank bit for bit, runs are deterministic, and writes stay
+inside their outputs."""
+import numpy as np
+import pytest
+import torch
+
+import long_context_exact_amd as ra
+import oracle
+from gpu_helpers import (check, fmt, from_dev, log, qkv, scale_bf16, shard, to_dev, unshard)
+
+pytestmark = pytest.mark.gpu
+
+PREFILL = [  # B, S, Hq, Hkv, d, P, layout, causal, dtype
+    (1, 1024, 2, 2, 64, 4, "contiguous", False, "f32"),
+    (1, 1024, 2, 2, 64, 4, "contiguous", True, "f32"),
+    (1, 520, 4, 2, 64, 4, "zigzag", True, "f32"),       # chunks of 65: ragged tiles
+    (2, 384, 2, 1, 128, 3, "zigzag", True, "f32"),
+    (1, 2048, 8, 8, 128, 8, "contiguous", True, "bf16"),
+    (2, 640, 4, 2, 128, 4, "zigzag", True, "bf16"),     # chunks of 80
+    (1, 96, 3, 1, 64, 3, "contiguous", True, "bf16"),   # shards of 32
+    (2, 1200, 4, 4, 128, 5, "zigzag", False, "bf16"),   # chunks of 120
+    (1, 300, 2, 2, 128, 1, "contiguous", True, "bf16"), # one rank
+    (1, 300, 2, 2, 64, 1, "zigzag", True, "bf16"),      # one rank, two chunks
+    (1, 512, 2, 2, 64, 16, "zigzag", True, "bf16"),     # chunks of 16
+    (1, 4096, 8, 2, 128, 4, "zigzag", True, "bf16"),    # GQA, chunks of 512
+]
+
+
+def _id(c):
+    B, S, Hq, Hkv, d, P, lay, causal, dt = c
+    return f"B{B}-S{S}-Hq{Hq}-Hkv{Hkv}-d{d}-P{P}-{lay}-{'causal' if causal else 'full'}-{dt}"
+
+
+def _run_prefill(Qn, Kn, Vn, P, layout, causal, dtype):
+    B, S, Hq, d = Qn.shape
+    Qs, Ks, Vs = (to_dev(shard(x, S, P, layout)) for x in (Qn, Kn, Vn))
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    O = torch.empty(B, S, Hq, d, dtype=tdt, device="cuda")
+    L = torch.empty(B, Hq, S, dtype=torch.float32, device="cuda")
+    ra.ra_fwd_all(Qs, Ks, Vs, O, L, P, causal, layout)
+    torch.cuda.synchronize()
+    return (Qs, Ks, Vs), O, L
+
+
+@pytest.mark.parametrize("case", PREFILL, ids=[_id(c) for c in PREFILL])
+def test_prefill_parity(case):
+    B, S, Hq, Hkv, d, P, layout, causal, dtype = case
+    log(f"prefill {_id(case)}")
+    Qn, Kn, Vn = qkv(B, S, S, Hq, Hkv, d, dtype, (1000, S, P))
+    (Qs, Ks, Vs), O, L = _run_prefill(Qn, Kn, Vn, P, layout, causal, dtype)
+    O_ref, lse_ref = oracle.attention(Qn, Kn, Vn, causal)
+    O_nat = unshard(from_dev(O), S, P, layout, axis=1)
+    L_nat = unshard(from_dev(L), S, P, layout, axis=2)
+    e = check(O_nat, O_ref, L_nat, lse_ref, dtype, _id(case))
+    log(f"  ok {fmt(e)}")
+
+    # every rank alone gives the same rows bit for bit
+    n = S // P
+    for r in range(P):
+        Qr = Qs[:, r * n:(r + 1) * n].contiguous()
+        Or = torch.empty_like(Qr)
+        Lr = torch.empty(B, Hq, n, dtype=torch.float32, device="cuda")
+        ra.ra_fwd_rank(Qr, Ks, Vs, Or, Lr, P, r, causal, layout)
+        torch.cuda.synchronize()
+        assert torch.equal(Or.view(torch.int16) if dtype == "bf16" else Or,
+                           O[:, r * n:(r + 1) * n].view(torch.int16) if dtype == "bf16"
+                           else O[:, r * n:(r + 1) * n]), f"rank {r} differs from ra_fwd_all"
+        assert torch.equal(Lr, L[:, :, r * n:(r + 1) * n])
+
+    # deterministic
+    _, O2, L2 = _run_prefill(Qn, Kn, Vn, P, layout, causal, dtype)
+    assert torch.equal(O.view(torch.int16) if dtype == "bf16" else O,
+                       O2.view(torch.int16) if dtype == "bf16" else O2)
+    assert torch.equal(L, L2)
+
+
+STRESS = ["peaky", "late_max", "zero_q"]
+
+
+@pytest.mark.parametrize("kind", STRESS)
+@pytest.mark.parametrize("layout", ["contiguous", "zigzag"])
+def test_prefill_stress_inputs(kind, layout):
+    B, S, Hq, Hkv, d, P = 1, 1024, 4, 2, 128, 4
+    log(f"stress {kind} {layout}")
+    Qn, Kn, Vn = qkv(B, S, S, Hq, Hkv, d, "bf16", (1100, len(kind)))
+    if kind == "peaky":      # large scores: big rescales between tiles
+        Qn = scale_bf16(Qn, 8.0)
+    elif kind == "late_max":  # a dominant key in the last shard of the ring order
+        last = oracle.natural_positions(S, P, layout)[(S // P) * 1 + 3]
+        Kn = Kn.copy()
+        Kn[:, last] = scale_bf16(Kn[:, last], 6.0)
+        Qn = scale_bf16(Qn, 3.0)
+    else:
+        Qn = np.zeros_like(Qn)
+    _, O, L = _run_prefill(Qn, Kn, Vn, P, layout, True, "bf16")
+    O_ref, lse_ref = oracle.attention(Qn, Kn, Vn, True)
+    e = check(unshard(from_dev(O), S, P, layout), O_ref,
+              unshard(from_dev(L), S, P, layout, axis=2), lse_ref, "bf16", kind)
+    log(f"  ok {fmt(e)}")
+
+
+def test_prefill_output_guard_bands():
+    B, S, Hq, Hkv, d, P, layout = 1, 640, 4, 2, 128, 4, "zigzag"
+    Qn, Kn, Vn = qkv(B, S, S, Hq, Hkv, d, "bf16", (1200,))
+    Qs, Ks, Vs = (to_dev(shard(x, S, P, layout)) for x in (Qn, Kn, Vn))
+    g = 4096
+    n_o, n_l = B * S * Hq * d, B * Hq * S
+    Obuf = torch.full((n_o + 2 * g,), 7.0, dtype=torch.bfloat16, device="cuda")
+    Lbuf = torch.full((n_l + 2 * g,), 7.0, dtype=torch.float32, device="cuda")
+    O = Obuf[g:g + n_o].view(B, S, Hq, d)
+    L = Lbuf[g:g + n_l].view(B, Hq, S)
+    ra.ra_fwd_all(Qs, Ks, Vs, O, L, P, True, layout)
+    torch.cuda.synchronize()
+    for buf, n in ((Obuf, n_o), (Lbuf, n_l)):
+        assert torch.all(buf[:g] == 7.0) and torch.all(buf[g + n:] == 7.0)
+
+
+DECODE = [  # B, Sq, Hq, Hkv, d, Skv, n_parts, dtype
+    (2, 1, 8, 2, 128, 1000, 3, "bf16"),
+    (1, 2, 8, 1, 64, 777, 5, "bf16"),      # 16 query rows per kv head
+    (1, 1, 32, 1, 128, 4099, 4, "bf16"),   # 32 rows: the full MFMA width
+    (3, 1, 4, 4, 128, 70, 8, "f32"),
+    (1, 1, 8, 2, 64, 5, 8, "bf16"),        # more parts than keys: empty parts
+    (2, 1, 16, 2, 128, 2048, 1, "f32"),
+]
+
+
+@pytest.mark.parametrize("case", DECODE, ids=[str(c) for c in DECODE])
+def test_decode_partials_and_merge(case):
+    B, Sq, Hq, Hkv, d, Skv, n_parts, dtype = case
+    log(f"decode {case}")
+    Qn, Kn, Vn = qkv(B, Sq, Skv, Hq, Hkv, d, dtype, (1300, Skv))
+    Q, K, V = to_dev(Qn), to_dev(Kn), to_dev(Vn)
+    rows = B * Sq * Hq
+    Op = torch.empty(n_parts, rows, d, dtype=torch.float32, device="cuda")
+    lp = torch.empty(n_parts, rows, dtype=torch.float32, device="cuda")
+    ra.ra_attn_partial(Q, K, V, Op, lp, n_parts)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    O = torch.empty(rows, d, dtype=tdt, device="cuda")
+    lse = torch.empty(rows, dtype=torch.float32, device="cuda")
+    ra.ra_merge_partials(Op, lp, O, lse)
+    torch.cuda.synchronize()
+
+    # each part against the oracle on its own key range
+    plen = -(-Skv // n_parts)
+    Op_h, lp_h = from_dev(Op), from_dev(lp)
+    for p in range(n_parts):
+        a, b = min(Skv, p * plen), min(Skv, (p + 1) * plen)
+        if a == b:
+            assert np.all(Op_h[p] == 0) and np.all(lp_h[p] == -np.inf)
+            continue
+        o_ref, l_ref = oracle.attention(Qn, Kn[:, a:b], Vn[:, a:b], False)
+        check(Op_h[p].reshape(B, Sq, Hq, d), o_ref, lp_h[p].reshape(B, Sq, Hq).transpose(0, 2, 1),
+              l_ref, "f32" if dtype == "f32" else "bf16", f"part {p}")
+    O_ref, lse_ref = oracle.attention(Qn, Kn, Vn, False)
+    e = check(from_dev(O).reshape(B, Sq, Hq, d), O_ref,
+              from_dev(lse).reshape(B, Sq, Hq).transpose(0, 2, 1), lse_ref, dtype, "merged")
+    log(f"  ok {fmt(e)}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_merge_kernel_vs_oracle(d, out):
+    rng = np.random.default_rng([1400, d])
+    n_parts, rows = 7, 1000
+    Op = rng.standard_normal((n_parts, rows, d)).astype(np.float32)
+    lp = (rng.standard_normal((n_parts, rows)) * 5).astype(np.float32)
+    lp[rng.random((n_parts, rows)) < 0.2] = -np.inf   # empty shards
+    lp[:, :3] = -np.inf                                # rows with no key at all
+    O = torch.empty(rows, d, dtype=torch.bfloat16 if out == "bf16" else torch.float32, device="cuda")
+    lse = torch.empty(rows, dtype=torch.float32, device="cuda")
+    ra.ra_merge_partials(to_dev(Op), to_dev(lp), O, lse)
+    O_ref, l_ref = oracle.merge(Op.astype(np.float64), lp.astype(np.float64))
+    O_g, l_g = from_dev(O), from_dev(lse)
+    assert np.all(O_g[:3] == 0) and np.all(l_g[:3] == -np.inf)
+    fin = np.isfinite(l_ref)
+    assert np.array_equal(np.isfinite(l_g), fin)
+    if out == "f32":
+        assert np.abs(O_g - O_ref).max() <= 1e-6 * max(1.0, np.abs(O_ref).max())
+    else:  # one bf16 rounding of the output
+        assert np.all(np.abs(O_g - O_ref) <= np.abs(O_ref) * 2.0 ** -8 + 1e-6)
+    assert np.abs(l_g[fin] - l_ref[fin]).max() <= 1e-6 * max(1.0, np.abs(l_ref[fin]).max())
+
+
+@pytest.mark.parametrize("inner", [16, 4, 6, 256])
+@pytest.mark.parametrize("layout", ["contiguous", "zigzag"])
+def test_layout_gather_bit_exact(inner, layout):
+    outer, S, P = 3, 96, 4
+    rng = np.random.default_rng([1500, inner])
+    x = rng.integers(0, 256, size=(outer, S, inner), dtype=np.uint8)
+    src = torch.from_numpy(x).cuda()
+    dst = torch.empty_like(src)
+    back = torch.empty_like(src)
+    ra.ra_layout_gather(src, dst, S, P, layout, inverse=False)
+    ra.ra_layout_gather(dst, back, S, P, layout, inverse=True)
+    torch.cuda.synchronize()
+    expect = x[:, oracle.natural_positions(S, P, layout)]
+    assert np.array_equal(dst.cpu().numpy(), expect)
+    assert np.array_equal(back.cpu().numpy(), x)
