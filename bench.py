@@ -1,0 +1,243 @@
+#!/usr/bin/env python3
+"""Benchmark of the ring-attention hot path on one MI355X.
+
+One step runs every stage of the path once, on synthetic inputs already
+resident in HBM:
+  1. layout: natural -> zig-zag sharded order of Q, K, V (ra_layout_gather)
+     for the 128k-token GQA workload (B1 Hq32 Hkv8 d128 S131072, P8);
+  2. prefill: rank 0's share of ring attention on that workload (ra_fwd_rank:
+     16384 local queries x 32 heads against all 131072 keys, visited in ring
+     order, causal, zig-zag);
+  3. decode: KV-sharded decode (B8, 1 query, Hq64 Hkv8 d128, 1,048,576 keys
+     per sequence; 8 shards, each split into 8 parts) -> per-part partials
+     (ra_attn_partial), then ra_merge_partials.
+Each stage is timed with HIP events on the stream the kernels run on.
+
+The printed JSON line reports ring-attention forward TFLOP/s (exact causal
+FLOPs, 4*d per scored (query, key) pair and head) as ``value``, with its
+roofline against the dense bf16 MFMA peak, and the decode path's HBM GB/s in
+the ``decode`` object.  ``cpu_baseline`` times the fp64 CPU oracle on a sample
+of the same prefill workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "ring-attn fwd TFLOP/s (% bf16 MFMA peak); KV-shard decode GB/s (% HBM peak)"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+PREFILL_SOURCES = ["fwd_bf16.hip", "attn_tile.h", "ra_device.h", "ra_internal.h"]
+DECODE_SOURCES = ["decode.hip", "attn_tile.h", "ra_device.h", "ra_internal.h"]
+
+
+def log(msg: str) -> None:
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def source_hash(files) -> str:
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "long_context_exact_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, files):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when the kernel source changed since the counters were taken."""
+    try:
+        data = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    rec = data.get(kernel)
+    if not rec or rec.get("source_hash") != source_hash(files):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, rank: int, n_rows: int):
+    """The fp64 oracle on a bounded sample of the prefill workload: n_rows
+    query rows of ``rank`` (half from each of its two zig-zag chunks, evenly
+    spaced), every query head, each row scored against all the keys it may
+    see.  Returns TFLOP/s in the same FLOP convention as the GPU figure."""
+    import numpy as np
+
+    import oracle
+    from long_context_exact_amd import synthetic
+
+    Q = synthetic.normal_tensor(w.q_shape, w.seed(0), "bf16")
+    K = synthetic.normal_tensor(w.kv_shape, w.seed(1), "bf16")
+    V = synthetic.normal_tensor(w.kv_shape, w.seed(2), "bf16")
+    c = w.S // (2 * w.P)
+    rows = []
+    for ch in (rank, 2 * w.P - 1 - rank):
+        rows += list(np.linspace(ch * c, (ch + 1) * c - 1, n_rows // 2).astype(np.int64))
+    rows = np.asarray(rows, dtype=np.int64)
+    flops = 4 * w.d * w.Hq * int(np.sum(rows + 1))
+    t0 = time.perf_counter()
+    oracle.attention_rows(Q, K, V, True, np.zeros_like(rows), rows)
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{len(rows)} query rows of rank {rank} (half from each of its two chunks), "
+                      f"all {w.Hq} heads, {flops / 1e9:.1f} GFLOP, {dt:.1f} s wall"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--rank", type=int, default=0, help="prefill rank whose share is timed")
+    ap.add_argument("--decode-parts", type=int, default=64)
+    ap.add_argument("--cpu-rows", type=int, default=128)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", choices=["all", "prefill", "decode"], default="all")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (--gpus {args.gpus} requested): the ring is "
+              "simulated on a single MI355X, with every shard resident; no multi-GPU run exists.",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    import long_context_exact_amd as ra
+    from long_context_exact_amd import synthetic
+    from long_context_exact_amd.workloads import WORKLOADS, decode_bytes, prefill_flops
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    ra.lib()
+    dev = torch.device("cuda:0")
+    do_pre = args.workload in ("all", "prefill")
+    do_dec = args.workload in ("all", "decode")
+    wp, wd = WORKLOADS[4], WORKLOADS[5]
+
+    launches = []  # (stage, fn)
+    if do_pre:
+        log(f"generating prefill inputs {wp.name}")
+        Qn = synthetic.to_device(wp.q_shape, wp.seed(0), "bf16", dev)
+        Kn = synthetic.to_device(wp.kv_shape, wp.seed(1), "bf16", dev)
+        Vn = synthetic.to_device(wp.kv_shape, wp.seed(2), "bf16", dev)
+        Qs, Ks, Vs = torch.empty_like(Qn), torch.empty_like(Kn), torch.empty_like(Vn)
+        n = wp.S // wp.P
+        r = args.rank
+        Q_r = Qs[:, r * n:(r + 1) * n]
+        O_r = torch.empty(Q_r.shape, dtype=torch.float32, device=dev)  # fp32 accumulator output
+        L_r = torch.empty(wp.B, wp.Hq, n, dtype=torch.float32, device=dev)
+
+        def layout():
+            for a, b in ((Qn, Qs), (Kn, Ks), (Vn, Vs)):
+                ra.ra_layout_gather(a, b, wp.S, wp.P, "zigzag", inverse=False)
+
+        def prefill():
+            ra.ra_fwd_rank(Q_r, Ks, Vs, O_r, L_r, wp.P, r, True, "zigzag")
+
+        launches += [("layout", layout), ("prefill", prefill)]
+    if do_dec:
+        log(f"generating decode inputs {wd.name} (2 x 16 GiB)")
+        Qd = synthetic.to_device(wd.q_shape, wd.seed(0), "bf16", dev)
+        Kd = synthetic.to_device(wd.kv_shape, wd.seed(1), "bf16", dev)
+        Vd = synthetic.to_device(wd.kv_shape, wd.seed(2), "bf16", dev)
+        parts = args.decode_parts
+        rows = wd.B * wd.Sq * wd.Hq
+        Op = torch.empty(parts, rows, wd.d, dtype=torch.float32, device=dev)
+        lp = torch.empty(parts, rows, dtype=torch.float32, device=dev)
+        Od = torch.empty(rows, wd.d, dtype=torch.float32, device=dev)
+        ld = torch.empty(rows, dtype=torch.float32, device=dev)
+
+        def decode():
+            ra.ra_attn_partial(Qd, Kd, Vd, Op, lp, parts)
+
+        def merge():
+            ra.ra_merge_partials(Op, lp, Od, ld)
+
+        launches += [("decode", decode), ("merge", merge)]
+    torch.cuda.synchronize()
+
+    def step(events=None):
+        for i, (_, fn) in enumerate(launches):
+            if events is not None:
+                events[i][0].record()
+            fn()
+            if events is not None:
+                events[i][1].record()
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in launches] for _ in range(args.steps)]
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(ev[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = {name: sum(ev[k][i][0].elapsed_time(ev[k][i][1]) for k in range(args.steps)) / args.steps
+          for i, (name, _) in enumerate(launches)}
+    log("stage ms: " + ", ".join(f"{k}={v:.3f}" for k, v in ms.items()))
+
+    out = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": wall * 1e3 / args.steps, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic i.i.d. N(0,1) inputs rounded to bf16 (seeded numpy PCG64)"}
+    cfg = {}
+    if do_pre:
+        flops = prefill_flops(wp, rank=args.rank)
+        tflops = flops / (ms["prefill"] * 1e-3) / 1e12
+        lay_bytes = 2 * 2 * (wp.B * wp.S * (wp.Hq + 2 * wp.Hkv) * wp.d)  # read + write, bf16
+        out.update({"value": tflops, "unit": "TFLOP/s"})
+        out["roofline"] = {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS,
+                           "unit": "TFLOP/s", "frac": tflops / PEAK_BF16_TFLOPS,
+                           "traffic": measured_traffic("prefill", PREFILL_SOURCES),
+                           "kernel": "fwd_bf16_kernel<128>", "flops_per_launch": flops,
+                           "ms_per_launch": ms["prefill"]}
+        out["layout"] = {"value": lay_bytes / (ms["layout"] * 1e-3) / 1e9, "unit": "GB/s",
+                         "ms": ms["layout"], "bytes": lay_bytes,
+                         "frac_hbm": lay_bytes / (ms["layout"] * 1e-3) / 1e9 / PEAK_HBM_GBS}
+        cfg.update({"workload": f"{wp.name} rank-{args.rank} share", "global_batch": wp.B,
+                    "seq_len": wp.S, "heads_q": wp.Hq, "heads_kv": wp.Hkv, "head_dim": wp.d,
+                    "ranks": wp.P, "layout": "zigzag", "causal": True})
+    if do_dec:
+        nb = decode_bytes(wd, args.decode_parts)
+        gbs = nb["attn_partial"] / (ms["decode"] * 1e-3) / 1e9
+        tot = nb["total"] / ((ms["decode"] + ms["merge"]) * 1e-3) / 1e9
+        out["decode"] = {"value": tot, "unit": "GB/s", "frac_hbm": tot / PEAK_HBM_GBS,
+                         "ms": ms["decode"] + ms["merge"],
+                         "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS,
+                                      "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+                                      "traffic": measured_traffic("decode", DECODE_SOURCES),
+                                      "kernel": "decode_bf16_kernel<128>",
+                                      "bytes_per_launch": nb["attn_partial"],
+                                      "ms_per_launch": ms["decode"]},
+                         "merge_ms": ms["merge"], "parts": args.decode_parts}
+        cfg["decode_workload"] = wd.name
+        if not do_pre:
+            out.update({"value": tot, "unit": "GB/s", "roofline": out["decode"]["roofline"]})
+            cfg["workload"] = wd.name
+    cfg["parallelism"] = "simulated ring (8 ranks resident on 1 GPU)"
+    out["config"] = cfg
+    if do_pre and not args.no_cpu_baseline:
+        log(f"cpu baseline: oracle on {args.cpu_rows} sampled rows")
+        out["cpu_baseline"] = cpu_baseline(wp, args.rank, args.cpu_rows)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

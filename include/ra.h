@@ -30,7 +30,10 @@
  *   - Layouts are row-major with the last dimension contiguous.  Sequence
  *     tensors are [B, S, H, d]; d (head dimension) is 64 or 128.
  *   - dtype: RA_DTYPE_F32 (float) or RA_DTYPE_BF16 (bfloat16 bit patterns,
- *     uint16).  Q, K, V and O share the dtype.  LSE and partials are fp32.
+ *     uint16) for Q, K and V.  The attention output O has its own o_dtype:
+ *     with bf16 inputs it may be bf16 (rounded to nearest even) or fp32 (the
+ *     fp32 accumulator, unrounded); with fp32 inputs it is fp32.  LSE and
+ *     partials are fp32.
  *   - The softmax scale is 1/sqrt(d) ([L8] section 1).
  *   - Grouped-query attention: query head h reads key/value head
  *     h / (Hq/Hkv) (contiguous groups; Hq must be a multiple of Hkv).
@@ -86,9 +89,9 @@ typedef enum { RA_DTYPE_F32 = 0, RA_DTYPE_BF16 = 1 } ra_dtype;
  *
  *   Q_r   [B, S/P, Hq, d]   the rank's local queries (its shard of Q)
  *   K, V  [B, S, Hkv, d]    all P shards, in sharded order
- *   O_r   [B, S/P, Hq, d]   output, same dtype as Q
+ *   O_r   [B, S/P, Hq, d]   output in o_dtype
  *   LSE_r [B, Hq, S/P]      fp32 output
- *   causal: 0 or 1; layout: ra_layout; dtype: ra_dtype.
+ *   causal: 0 or 1; layout: ra_layout; dtype, o_dtype: ra_dtype.
  * Requirements: S % P == 0 (contiguous) or S % (2P) == 0 (zig-zag);
  * 0 <= rank < P; Hq % Hkv == 0; d in {64, 128}.  Q_r/O_r must not alias K/V.
  * For B == 1, Q_r/O_r may point at rows rank*S/P of full sharded tensors.
@@ -96,7 +99,7 @@ typedef enum { RA_DTYPE_F32 = 0, RA_DTYPE_BF16 = 1 } ra_dtype;
  */
 int ra_fwd_rank(const void* Q_r, const void* K, const void* V, void* O_r, float* LSE_r,
                 int B, int Hq, int Hkv, int64_t S, int d, int P, int rank,
-                int causal, int layout, int dtype, void* stream);
+                int causal, int layout, int dtype, int o_dtype, void* stream);
 
 /*
  * ra_fwd_all -- all P simulated ranks in one launch.
@@ -106,7 +109,7 @@ int ra_fwd_rank(const void* Q_r, const void* K, const void* V, void* O_r, float*
  */
 int ra_fwd_all(const void* Q, const void* K, const void* V, void* O, float* LSE,
                int B, int Hq, int Hkv, int64_t S, int d, int P,
-               int causal, int layout, int dtype, void* stream);
+               int causal, int layout, int dtype, int o_dtype, void* stream);
 
 /*
  * ra_merge_partials -- combine (O, lse) partials that were computed over

@@ -43,8 +43,9 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         vp, i32, i64, fp = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_void_p
         L.ra_fwd_rank.argtypes = [vp, vp, vp, vp, fp, i32, i32, i32, i64, i32, i32, i32, i32, i32,
-                                  i32, vp]
-        L.ra_fwd_all.argtypes = [vp, vp, vp, vp, fp, i32, i32, i32, i64, i32, i32, i32, i32, i32, vp]
+                                  i32, i32, vp]
+        L.ra_fwd_all.argtypes = [vp, vp, vp, vp, fp, i32, i32, i32, i64, i32, i32, i32, i32, i32, i32,
+                                 vp]
         L.ra_merge_partials.argtypes = [fp, fp, vp, fp, i32, i64, i32, i32, vp]
         L.ra_attn_partial.argtypes = [vp, vp, vp, fp, fp, i32, i32, i32, i64, i64, i32, i32, i32, vp]
         L.ra_layout_gather.argtypes = [vp, vp, i64, i64, i64, i32, i32, i32, vp]
@@ -100,7 +101,8 @@ def _layout(layout) -> int:
 
 def ra_fwd_rank(Q_r, K, V, O_r, LSE_r, P: int, rank: int, causal: bool, layout, stream=None):
     """One simulated rank: Q_r/O_r [B, S/P, Hq, d], K/V [B, S, Hkv, d] (all P
-    shards, sharded order), LSE_r [B, Hq, S/P] float32."""
+    shards, sharded order), LSE_r [B, Hq, S/P] float32.  O_r may be float32
+    or, for bf16 inputs, bfloat16."""
     B, S, Hkv, d = K.shape
     Hq = Q_r.shape[2]
     if tuple(Q_r.shape) != (B, S // P, Hq, d) or O_r.shape != Q_r.shape or V.shape != K.shape:
@@ -108,16 +110,17 @@ def ra_fwd_rank(Q_r, K, V, O_r, LSE_r, P: int, rank: int, causal: bool, layout, 
     if tuple(LSE_r.shape) != (B, Hq, S // P) or LSE_r.dtype != _torch().float32:
         raise ValueError("LSE_r must be float32 [B, Hq, S/P]")
     dt = _dtype_code(Q_r)
-    if not (K.dtype == V.dtype == O_r.dtype == Q_r.dtype):
-        raise TypeError("Q, K, V, O must share a dtype")
+    if not (K.dtype == V.dtype == Q_r.dtype):
+        raise TypeError("Q, K, V must share a dtype")
     _check(lib().ra_fwd_rank(_dev(Q_r, "Q_r"), _dev(K, "K"), _dev(V, "V"), _dev(O_r, "O_r"),
                              _dev(LSE_r, "LSE_r"), B, Hq, Hkv, S, d, P, rank, int(bool(causal)),
-                             _layout(layout), dt, _stream(stream)))
+                             _layout(layout), dt, _dtype_code(O_r), _stream(stream)))
 
 
 def ra_fwd_all(Q, K, V, O, LSE, P: int, causal: bool, layout, stream=None):
     """All P simulated ranks: Q/O [B, S, Hq, d], K/V [B, S, Hkv, d],
-    LSE [B, Hq, S] float32, sharded order."""
+    LSE [B, Hq, S] float32, sharded order.  O may be float32 or, for bf16
+    inputs, bfloat16."""
     B, S, Hkv, d = K.shape
     Hq = Q.shape[2]
     if tuple(Q.shape) != (B, S, Hq, d) or O.shape != Q.shape or V.shape != K.shape:
@@ -125,11 +128,11 @@ def ra_fwd_all(Q, K, V, O, LSE, P: int, causal: bool, layout, stream=None):
     if tuple(LSE.shape) != (B, Hq, S) or LSE.dtype != _torch().float32:
         raise ValueError("LSE must be float32 [B, Hq, S]")
     dt = _dtype_code(Q)
-    if not (K.dtype == V.dtype == O.dtype == Q.dtype):
-        raise TypeError("Q, K, V, O must share a dtype")
+    if not (K.dtype == V.dtype == Q.dtype):
+        raise TypeError("Q, K, V must share a dtype")
     _check(lib().ra_fwd_all(_dev(Q, "Q"), _dev(K, "K"), _dev(V, "V"), _dev(O, "O"),
                             _dev(LSE, "LSE"), B, Hq, Hkv, S, d, P, int(bool(causal)),
-                            _layout(layout), dt, _stream(stream)))
+                            _layout(layout), dt, _dtype_code(O), _stream(stream)))
 
 
 def ra_merge_partials(O_parts, lse_parts, O, lse=None, stream=None):

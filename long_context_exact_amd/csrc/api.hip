@@ -32,7 +32,8 @@ int hip_status(hipError_t e, const char* what) {
 
 // Checks shared by ra_fwd_rank and ra_fwd_all.
 int check_fwd(const void* Q, const void* K, const void* V, const void* O, const float* LSE, int B,
-              int Hq, int Hkv, int64_t S, int d, int P, int causal, int layout, int dtype) {
+              int Hq, int Hkv, int64_t S, int d, int P, int causal, int layout, int dtype,
+              int o_dtype) {
     if (!Q || !K || !V || !O || !LSE) return fail(RA_ERR_INVALID_ARG, "null tensor pointer");
     if (B <= 0 || Hq <= 0 || Hkv <= 0 || S <= 0 || P <= 0)
         return fail(RA_ERR_INVALID_ARG, "sizes must be positive (B=%d Hq=%d Hkv=%d S=%lld P=%d)", B,
@@ -42,6 +43,10 @@ int check_fwd(const void* Q, const void* K, const void* V, const void* O, const 
         return fail(RA_ERR_INVALID_ARG, "unknown layout %d", layout);
     if (dtype != RA_DTYPE_F32 && dtype != RA_DTYPE_BF16)
         return fail(RA_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+    if (o_dtype != RA_DTYPE_F32 && o_dtype != RA_DTYPE_BF16)
+        return fail(RA_ERR_INVALID_ARG, "unknown output dtype %d", o_dtype);
+    if (dtype == RA_DTYPE_F32 && o_dtype != RA_DTYPE_F32)
+        return fail(RA_ERR_UNSUPPORTED, "fp32 inputs need an fp32 output");
     if (d != 64 && d != 128) return fail(RA_ERR_UNSUPPORTED, "head dim %d (supported: 64, 128)", d);
     if (Hq % Hkv != 0) return fail(RA_ERR_UNSUPPORTED, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
     if (layout == RA_LAYOUT_CONTIGUOUS && S % P != 0)
@@ -55,7 +60,7 @@ int check_fwd(const void* Q, const void* K, const void* V, const void* O, const 
 
 ra::FwdParams plan_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int B,
                        int Hq, int Hkv, int64_t S, int d, int P, int causal, int layout, int dtype,
-                       int rank_lo, int n_ranks, int q_local) {
+                       int o_dtype, int rank_lo, int n_ranks, int q_local) {
     ra::FwdParams p;
     p.Q = Q;
     p.K = K;
@@ -73,6 +78,7 @@ ra::FwdParams plan_fwd(const void* Q, const void* K, const void* V, void* O, flo
     p.G = Hq / Hkv;
     p.P = P;
     p.causal = causal;
+    p.o_f32 = o_dtype == RA_DTYPE_F32;
     p.rank_lo = rank_lo;
     p.n_ranks = n_ranks;
     p.q_local = q_local;
@@ -101,20 +107,22 @@ extern "C" {
 
 int ra_fwd_rank(const void* Q_r, const void* K, const void* V, void* O_r, float* LSE_r, int B,
                 int Hq, int Hkv, int64_t S, int d, int P, int rank, int causal, int layout, int dtype,
-                void* stream) {
-    int rc = check_fwd(Q_r, K, V, O_r, LSE_r, B, Hq, Hkv, S, d, P, causal, layout, dtype);
+                int o_dtype, void* stream) {
+    int rc = check_fwd(Q_r, K, V, O_r, LSE_r, B, Hq, Hkv, S, d, P, causal, layout, dtype, o_dtype);
     if (rc != RA_OK) return rc;
     if (rank < 0 || rank >= P) return fail(RA_ERR_INVALID_ARG, "rank %d outside [0, %d)", rank, P);
     ra::FwdParams p = plan_fwd(Q_r, K, V, O_r, LSE_r, B, Hq, Hkv, S, d, P, causal, layout, dtype,
-                               rank, 1, 1);
+                               o_dtype, rank, 1, 1);
     return launch_fwd(p, d, dtype, stream);
 }
 
 int ra_fwd_all(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int Hq,
-               int Hkv, int64_t S, int d, int P, int causal, int layout, int dtype, void* stream) {
-    int rc = check_fwd(Q, K, V, O, LSE, B, Hq, Hkv, S, d, P, causal, layout, dtype);
+               int Hkv, int64_t S, int d, int P, int causal, int layout, int dtype, int o_dtype,
+               void* stream) {
+    int rc = check_fwd(Q, K, V, O, LSE, B, Hq, Hkv, S, d, P, causal, layout, dtype, o_dtype);
     if (rc != RA_OK) return rc;
-    ra::FwdParams p = plan_fwd(Q, K, V, O, LSE, B, Hq, Hkv, S, d, P, causal, layout, dtype, 0, P, 0);
+    ra::FwdParams p = plan_fwd(Q, K, V, O, LSE, B, Hq, Hkv, S, d, P, causal, layout, dtype, o_dtype,
+                               0, P, 0);
     return launch_fwd(p, d, dtype, stream);
 }
 

@@ -184,22 +184,24 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(FwdParams p) {
     const float l_tot = xor32_sum(l_run);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     if (qvalid) {
-        uint16_t* Op = (uint16_t*)p.O + ((qt.b * p.q_rows + qt.q_row0 + qi) * p.Hq + qt.qh) * (int64_t)D;
+        const int64_t obase = ((qt.b * p.q_rows + qt.q_row0 + qi) * p.Hq + qt.qh) * (int64_t)D;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
                 // accumulator registers 4*g4..4*g4+3 hold dims db*32 + 8*g4 + 4h + 0..3
                 const int dim = db * 32 + 8 * g4 + 4 * h;
-                __bf16 o0 = (__bf16)(oacc[db][4 * g4 + 0] * inv);
-                __bf16 o1 = (__bf16)(oacc[db][4 * g4 + 1] * inv);
-                __bf16 o2 = (__bf16)(oacc[db][4 * g4 + 2] * inv);
-                __bf16 o3 = (__bf16)(oacc[db][4 * g4 + 3] * inv);
-                const uint32_t w0 = (uint32_t)__builtin_bit_cast(uint16_t, o0) |
-                                    ((uint32_t)__builtin_bit_cast(uint16_t, o1) << 16);
-                const uint32_t w1 = (uint32_t)__builtin_bit_cast(uint16_t, o2) |
-                                    ((uint32_t)__builtin_bit_cast(uint16_t, o3) << 16);
-                *(uint2*)(Op + dim) = make_uint2(w0, w1);
+                const float o0 = oacc[db][4 * g4 + 0] * inv, o1 = oacc[db][4 * g4 + 1] * inv;
+                const float o2 = oacc[db][4 * g4 + 2] * inv, o3 = oacc[db][4 * g4 + 3] * inv;
+                if (p.o_f32) {
+                    *(float4*)((float*)p.O + obase + dim) = make_float4(o0, o1, o2, o3);
+                } else {
+                    const uint32_t w0 = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)o0) |
+                                        ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)o1) << 16);
+                    const uint32_t w1 = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)o2) |
+                                        ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)o3) << 16);
+                    *(uint2*)((uint16_t*)p.O + obase + dim) = make_uint2(w0, w1);
+                }
             }
         if (h == 0) {
             const float lse = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : kNegInf;

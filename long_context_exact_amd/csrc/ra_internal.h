@@ -27,6 +27,7 @@ struct FwdParams {
     int P;
     int zigzag;        // 0 contiguous, 1 zig-zag
     int causal;
+    int o_f32;         // 1: O is fp32, 0: O has the input dtype (bf16)
     int rank_lo;       // first rank of this launch
     int n_ranks;       // ranks in this launch (P for all, 1 for one rank)
     int q_local;       // 1: Q/O/LSE rows are rank-local (row 0 = first row of rank_lo)

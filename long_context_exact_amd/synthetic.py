@@ -70,3 +70,22 @@ def normal_range(seed: tuple, start: int, stop: int, dtype: str = "f32") -> np.n
 def normal_tensor(shape, seed: tuple, dtype: str = "f32") -> np.ndarray:
     n = int(np.prod(shape))
     return normal_range(seed, 0, n, dtype).reshape(shape)
+
+
+def to_device(shape, seed: tuple, dtype: str, device="cuda", block_chunks: int = 32):
+    """Generate a tensor block by block on the host and copy each block into a
+    device tensor (host memory stays bounded for multi-GiB tensors).  The bits
+    equal ``normal_tensor(shape, seed, dtype)``."""
+    import torch
+
+    n = int(np.prod(shape))
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    out = torch.empty(n, dtype=tdt, device=device)
+    step = CHUNK * block_chunks
+    for a in range(0, n, step):
+        b = min(n, a + step)
+        host = torch.from_numpy(normal_range(seed, a, b, dtype))
+        if dtype == "bf16":
+            host = host.view(torch.bfloat16)
+        out[a:b].copy_(host)
+    return out.view(*shape)

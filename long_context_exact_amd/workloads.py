@@ -74,7 +74,7 @@ def prefill_flops(w: Workload, rank: int | None = None) -> int:
     return 4 * w.d * w.Hq * w.B * pairs
 
 
-def decode_bytes(w: Workload, n_parts: int, elem_bytes: int = 2) -> dict:
+def decode_bytes(w: Workload, n_parts: int, elem_bytes: int = 2, out_bytes: int = 4) -> dict:
     """Algorithmic HBM bytes of one decode step (KV-sharded attention of one
     query per sequence, then the merge of the per-part partials):
 
@@ -86,7 +86,7 @@ def decode_bytes(w: Workload, n_parts: int, elem_bytes: int = 2) -> dict:
     kv = 2 * w.B * w.S * w.Hkv * w.d * elem_bytes
     q = rows * w.d * elem_bytes
     partials = n_parts * rows * (w.d + 1) * 4
-    out = rows * (w.d * elem_bytes + 4)
+    out = rows * (w.d * out_bytes + 4)
     return {"kv": kv, "q": q, "partials": partials, "out": out,
             "attn_partial": kv + q + partials,
             "merge": partials + out,

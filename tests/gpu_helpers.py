@@ -61,9 +61,13 @@ def unshard(x: np.ndarray, S: int, P: int, layout: str, axis: int = 1) -> np.nda
     return out
 
 
-def check(O, O_ref, lse, lse_ref, dtype: str, what: str = "") -> dict:
+def check(O, O_ref, lse, lse_ref, dtype: str, what: str = "", o_rounded: bool = False) -> dict:
     """Compare GPU results (float64 arrays) with the oracle's, element by
-    element, with the tolerances for the input dtype.  Returns the errors."""
+    element, with the tolerances for the input dtype.  Returns the errors.
+
+    o_rounded: O was stored in bf16.  Rounding to bf16 alone moves a value by
+    up to 2**-8 of its magnitude (0.0156 at |O| = 4), more than the 1e-2
+    bound, so that bound is widened by 2**-8 |O_ref| per element."""
     assert O.shape == O_ref.shape and lse.shape == lse_ref.shape
     assert np.all(np.isfinite(O)), f"{what}: non-finite O"
     fin = np.isfinite(lse_ref)
@@ -75,7 +79,11 @@ def check(O, O_ref, lse, lse_ref, dtype: str, what: str = "") -> dict:
         "lse_max": float(np.abs(lse[fin] - lse_ref[fin]).max()) if fin.any() else 0.0,
     }
     if dtype == "bf16":
-        ok = e["o_max"] <= BF16_O_MAX and e["o_rel_l2"] <= BF16_O_REL and e["lse_max"] <= BF16_LSE
+        if o_rounded:
+            e["o_excess"] = float((err - (BF16_O_MAX + 2.0 ** -8 * np.abs(O_ref))).max()) if err.size else -1.0
+            ok = e["o_excess"] <= 0 and e["o_rel_l2"] <= BF16_O_REL and e["lse_max"] <= BF16_LSE
+        else:
+            ok = e["o_max"] <= BF16_O_MAX and e["o_rel_l2"] <= BF16_O_REL and e["lse_max"] <= BF16_LSE
     else:
         ok = e["o_max"] <= F32_O_MAX and e["lse_max"] <= F32_LSE
     assert ok, f"{what}: parity failed {e}"

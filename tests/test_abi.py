@@ -42,11 +42,11 @@ def test_version():
 
 def _fwd_rank(**kw):
     a = dict(Q=FAKE, K=FAKE, V=FAKE, O=FAKE, L=FAKE, B=1, Hq=8, Hkv=8, S=8192, d=128, P=8,
-             rank=0, causal=1, layout=1, dtype=1)
+             rank=0, causal=1, layout=1, dtype=1, o_dtype=0)
     a.update(kw)
     return ra.lib().ra_fwd_rank(a["Q"], a["K"], a["V"], a["O"], a["L"], a["B"], a["Hq"], a["Hkv"],
                                 a["S"], a["d"], a["P"], a["rank"], a["causal"], a["layout"],
-                                a["dtype"], NULL)
+                                a["dtype"], a["o_dtype"], NULL)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -59,6 +59,8 @@ def _fwd_rank(**kw):
     (dict(causal=2), ra.RA_ERR_INVALID_ARG),
     (dict(layout=7), ra.RA_ERR_INVALID_ARG),
     (dict(dtype=5), ra.RA_ERR_INVALID_ARG),
+    (dict(o_dtype=3), ra.RA_ERR_INVALID_ARG),
+    (dict(dtype=0, o_dtype=1), ra.RA_ERR_UNSUPPORTED),     # fp32 inputs, bf16 output
     (dict(d=96), ra.RA_ERR_UNSUPPORTED),
     (dict(Hq=12, Hkv=8), ra.RA_ERR_UNSUPPORTED),
     (dict(S=8200), ra.RA_ERR_UNSUPPORTED),                 # 8200 % 16 != 0 under zig-zag
@@ -73,7 +75,7 @@ def test_fwd_rank_rejects(kw, code):
 
 def test_fwd_all_and_others_reject():
     L = ra.lib()
-    assert L.ra_fwd_all(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 4, 4, 1000, 64, 3, 0, 0, 0, NULL) \
+    assert L.ra_fwd_all(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 4, 4, 1000, 64, 3, 0, 0, 0, 0, NULL) \
         == ra.RA_ERR_UNSUPPORTED
     assert "equal shards" in ra.last_error()
     assert L.ra_merge_partials(FAKE, FAKE, FAKE, NULL, 0, 10, 128, 1, NULL) == ra.RA_ERR_INVALID_ARG

@@ -34,10 +34,10 @@ def _id(c):
     return f"B{B}-S{S}-Hq{Hq}-Hkv{Hkv}-d{d}-P{P}-{lay}-{'causal' if causal else 'full'}-{dt}"
 
 
-def _run_prefill(Qn, Kn, Vn, P, layout, causal, dtype):
+def _run_prefill(Qn, Kn, Vn, P, layout, causal, dtype, out="f32"):
     B, S, Hq, d = Qn.shape
     Qs, Ks, Vs = (to_dev(shard(x, S, P, layout)) for x in (Qn, Kn, Vn))
-    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    tdt = torch.bfloat16 if out == "bf16" else torch.float32
     O = torch.empty(B, S, Hq, d, dtype=tdt, device="cuda")
     L = torch.empty(B, Hq, S, dtype=torch.float32, device="cuda")
     ra.ra_fwd_all(Qs, Ks, Vs, O, L, P, causal, layout)
@@ -61,20 +61,25 @@ def test_prefill_parity(case):
     n = S // P
     for r in range(P):
         Qr = Qs[:, r * n:(r + 1) * n].contiguous()
-        Or = torch.empty_like(Qr)
+        Or = torch.empty(Qr.shape, dtype=O.dtype, device="cuda")
         Lr = torch.empty(B, Hq, n, dtype=torch.float32, device="cuda")
         ra.ra_fwd_rank(Qr, Ks, Vs, Or, Lr, P, r, causal, layout)
         torch.cuda.synchronize()
-        assert torch.equal(Or.view(torch.int16) if dtype == "bf16" else Or,
-                           O[:, r * n:(r + 1) * n].view(torch.int16) if dtype == "bf16"
-                           else O[:, r * n:(r + 1) * n]), f"rank {r} differs from ra_fwd_all"
+        assert torch.equal(Or, O[:, r * n:(r + 1) * n]), f"rank {r} differs from ra_fwd_all"
         assert torch.equal(Lr, L[:, :, r * n:(r + 1) * n])
 
     # deterministic
     _, O2, L2 = _run_prefill(Qn, Kn, Vn, P, layout, causal, dtype)
-    assert torch.equal(O.view(torch.int16) if dtype == "bf16" else O,
-                       O2.view(torch.int16) if dtype == "bf16" else O2)
+    assert torch.equal(O, O2)
     assert torch.equal(L, L2)
+
+    if dtype == "bf16":
+        # a bf16 output is the same fp32 result rounded to nearest even
+        _, Ob, Lb = _run_prefill(Qn, Kn, Vn, P, layout, causal, dtype, out="bf16")
+        assert torch.equal(Ob.view(torch.int16), O.to(torch.bfloat16).view(torch.int16))
+        assert torch.equal(Lb, L)
+        check(unshard(from_dev(Ob), S, P, layout, axis=1), O_ref, L_nat, lse_ref, dtype,
+              _id(case) + " bf16 out", o_rounded=True)
 
 
 STRESS = ["peaky", "late_max", "zero_q"]
@@ -108,7 +113,7 @@ def test_prefill_output_guard_bands():
     Qs, Ks, Vs = (to_dev(shard(x, S, P, layout)) for x in (Qn, Kn, Vn))
     g = 4096
     n_o, n_l = B * S * Hq * d, B * Hq * S
-    Obuf = torch.full((n_o + 2 * g,), 7.0, dtype=torch.bfloat16, device="cuda")
+    Obuf = torch.full((n_o + 2 * g,), 7.0, dtype=torch.float32, device="cuda")
     Lbuf = torch.full((n_l + 2 * g,), 7.0, dtype=torch.float32, device="cuda")
     O = Obuf[g:g + n_o].view(B, S, Hq, d)
     L = Lbuf[g:g + n_l].view(B, Hq, S)
@@ -138,11 +143,14 @@ def test_decode_partials_and_merge(case):
     Op = torch.empty(n_parts, rows, d, dtype=torch.float32, device="cuda")
     lp = torch.empty(n_parts, rows, dtype=torch.float32, device="cuda")
     ra.ra_attn_partial(Q, K, V, Op, lp, n_parts)
-    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
-    O = torch.empty(rows, d, dtype=tdt, device="cuda")
+    O = torch.empty(rows, d, dtype=torch.float32, device="cuda")
     lse = torch.empty(rows, dtype=torch.float32, device="cuda")
     ra.ra_merge_partials(Op, lp, O, lse)
+    Ob = torch.empty(rows, d, dtype=torch.bfloat16, device="cuda")
+    ra.ra_merge_partials(Op, lp, Ob)
     torch.cuda.synchronize()
+    # a bf16 output is the fp32 result rounded to nearest even
+    assert torch.equal(Ob.view(torch.int16), O.to(torch.bfloat16).view(torch.int16))
 
     # each part against the oracle on its own key range
     plen = -(-Skv // n_parts)
