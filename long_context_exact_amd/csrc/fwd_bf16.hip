@@ -1,49 +1,148 @@
 // fwd_bf16.hip -- blockwise ring-attention forward, bf16 inputs, gfx950 MFMA.
 //
-// One work-group owns a tile of 128 queries of one head (4 waves x 32
-// queries) and keeps its online-softmax state (m, l, O) in registers while
-// the key/value tiles of the P resident shards stream past it in ring order
-// (lesson 8 "Context Parallelism (CP)", sections 2 and 3).  Per key tile:
+// One work-group owns a tile of 256 queries of one head (8 waves x 32
+// queries, two waves per SIMD) and keeps its online-softmax state (m, l, O)
+// in registers while the key/value tiles of the P resident shards stream past
+// it in ring order (lesson 8 "Context Parallelism (CP)", sections 2 and 3).
+// Per key tile of 64 keys and per wave:
 //
 //   S^T = K Q^T          v_mfma_f32_32x32x16_bf16, fp32 accumulate
 //   mask                 only on tiles that cross the causal diagonal or the
 //                        ragged end of a chunk
-//   m~ = max(m, max S)   in-lane max over the lane's 32 scores + one swap with
-//                        the other half-wave (each lane owns one query)
-//   P = exp2(S*c - m~)   c = log2(e)/sqrt(d) folded into one FMA
-//   l = l*a + sum P      a = exp2(m - m~), lane-partial sums
+//   m~ = max(m, max S)   in-lane max over the lane's 32 scores + one
+//                        permlane32 swap (each lane owns one query)
+//   P = exp2(S*c - m')   c = log2(e)/sqrt(d) folded into one FMA
+//   l = l*a + sum P      lane-partial sums, a = exp2(m - m'); a second sum
+//                        of the bf16-rounded P (v_dot2 with ones) normalises O
 //   O^T = O^T*a + V^T P^T   v_mfma_f32_32x32x16_bf16 with P rounded to bf16
 //
-// The score matrix is produced transposed (keys along MFMA rows, queries
-// along columns) so each lane holds whole rows of its own query and the
-// softmax needs no cross-lane reduction beyond one half-wave swap.  The K
-// rows fed to the first MFMA are permuted (bits 2 and 3 of the row index
-// swapped) so that the accumulator hands every lane 8 consecutive keys per
-// 16-key block: exactly the B operand layout of the second MFMA, with no data
-// movement between the two products.
+// The reference point m' of the exponentials is moved only when the running
+// maximum has grown by more than 2^8 since the last move (then P <= 256):
+// O and l are always taken relative to the same m', so the result is the
+// same; the 64 multiplies of the O rescale are skipped on most tiles.
 //
-// K and V tiles (64 keys) are double-buffered in LDS.  Global loads for tile
-// i+1 are issued before the MFMAs of tile i.  K is stored row-major with a
-// 16-byte-chunk XOR swizzle; V is stored transposed (V^T, keys contiguous) so
-// the second MFMA's A operand is one 16-byte LDS read per lane.
-#include "attn_tile.h"
+// The score matrix is produced transposed (keys along MFMA rows, queries
+// along columns) so each lane holds whole rows of its own query.  The K rows
+// fed to the first MFMA are permuted (bits 2 and 3 of the row index swapped)
+// so the accumulator hands every lane 8 consecutive keys per 16-key block:
+// exactly the B operand of the second MFMA, with no data movement.  V stays
+// key-major in LDS and the PV operand (8 consecutive keys of one dim per
+// lane) is read with the gfx950 transpose load ds_read_b64_tr_b16.
+//
+// K and V tiles are double-buffered in LDS.  Each thread stages 1/512 of the
+// next tile in registers: tile i+1 is written to LDS and tile i+2's global
+// loads are issued before the MFMAs of tile i, so their latency hides behind
+// a whole tile of compute; one barrier per tile.
+#include "ra_device.h"
 
 namespace ra {
 namespace {
 
-constexpr int BM = FWD_BF16_BLOCK_M;  // queries per work-group
+constexpr int BM = FWD_BF16_BLOCK_M;  // queries per work-group (8 waves x 32)
 constexpr int BN = 64;                // keys per tile
-constexpr int NT = 256;               // threads per work-group
+constexpr int NT = 512;               // threads per work-group
+constexpr float kLazy = 8.0f;         // log2 headroom before the reference max moves
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 template <int D>
-__global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(FwdParams p) {
-    using T = Tile<D, BN, NT>;
+struct KvTile {
+    static constexpr int KCH = D / 8;              // 16-byte chunks per row
+    static constexpr int LOADS = BN * KCH / NT;    // 16-byte loads per thread per tensor
+    static constexpr int ELEMS = BN * D;
+    static_assert(LOADS >= 1 && BN * KCH % NT == 0, "tile split");
+
+    // K: chunk c of row r lives at chunk c ^ (r mod KCH): the 32 rows x 2
+    // chunks of one MFMA operand read hit every bank equally.
+    static __device__ __forceinline__ int k_off(int row, int ch) {
+        return row * D + ((ch ^ (row & (KCH - 1))) << 3);
+    }
+    // V: chunk c of row r lives at chunk c ^ s(r); one transpose read touches
+    // 8 rows (two groups of 4 consecutive) x 32 dims, spread over all banks.
+    static __device__ __forceinline__ int v_sw(int row) {
+        return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
+    }
+    static __device__ __forceinline__ int v_off(int row, int ch) {
+        return row * D + ((ch ^ v_sw(row)) << 3);
+    }
+
+    struct Regs {
+        uint4 k[LOADS];
+        uint4 v[LOADS];
+    };
+
+    // global -> registers; rows >= klen load as zero
+    static __device__ __forceinline__ void load(Regs& r, const uint16_t* Kb, const uint16_t* Vb,
+                                                int64_t row_stride, int klen, int t) {
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            const int id = t + NT * i;
+            const int row = id / KCH, ch = id % KCH;
+            const bool ok = row < klen;
+            const int64_t off = row * row_stride + ch * 8;
+            r.k[i] = ok ? *(const uint4*)(Kb + off) : make_uint4(0, 0, 0, 0);
+            r.v[i] = ok ? *(const uint4*)(Vb + off) : make_uint4(0, 0, 0, 0);
+        }
+    }
+    static __device__ __forceinline__ void store(const Regs& r, uint16_t* Ks, uint16_t* Vs, int t) {
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            const int id = t + NT * i;
+            const int row = id / KCH, ch = id % KCH;
+            *(uint4*)(Ks + k_off(row, ch)) = r.k[i];
+            *(uint4*)(Vs + v_off(row, ch)) = r.v[i];
+        }
+    }
+};
+
+__device__ __forceinline__ int swap_bits23(int m) {
+    return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
+}
+
+// max / sum of a value over the two half-waves (lanes l and l^32)
+__device__ __forceinline__ float halves_max(float x) {
+    const unsigned u = __builtin_bit_cast(unsigned, x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+    const unsigned u = __builtin_bit_cast(unsigned, x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
+
+__device__ __forceinline__ i16x4 ds_read_tr(const uint16_t* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
+}
+
+struct TileDesc {
+    int64_t krow;  // first K/V row (sharded order)
+    int64_t kpos;  // global position of that row
+    int klen;      // valid rows of the tile (ragged end of a chunk)
+};
+
+__device__ __forceinline__ TileDesc tile_desc(const FwdParams& p, const KvIter& it) {
+    TileDesc d;
+    const int64_t off = (int64_t)it.tile * BN;
+    d.krow = it.krow + off;
+    d.kpos = it.kpos + off;
+    const int64_t left = p.c - off;
+    d.klen = left < BN ? (int)left : BN;
+    return d;
+}
+
+template <int D>
+__global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdParams p) {
+    using T = KvTile<D>;
     constexpr int KB = D / 16;  // MFMA k-blocks of Q K^T
     constexpr int DB = D / 32;  // 32-dim blocks of O^T
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2][2 * T::ELEMS];
+    __shared__ __attribute__((aligned(16))) uint16_t ldsK[2][T::ELEMS];
+    __shared__ __attribute__((aligned(16))) uint16_t ldsV[2][T::ELEMS];
 
     const QTile qt = decode_qtile<BM>(p, blockIdx.x);
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int t = threadIdx.x;
+    const int lane = t & 63, w = t >> 6;
     const int h = lane >> 5, m = lane & 31;
 
     // this lane's query (MFMA column m of the wave's 32 queries)
@@ -55,10 +154,10 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(FwdParams p) {
     const int64_t wq_hi = wq_lo + (wrows < 32 ? wrows : 32) - 1;
     const int64_t qmax = qt.pos0 + qt.rows - 1;
 
-    const uint16_t* Q = (const uint16_t*)p.Q;
     bf16x8 qop[KB];
     {
-        const uint16_t* qp = Q + ((qt.b * p.q_rows + qt.q_row0 + qi) * p.Hq + qt.qh) * (int64_t)D;
+        const uint16_t* qp = (const uint16_t*)p.Q +
+                             ((qt.b * p.q_rows + qt.q_row0 + qi) * p.Hq + qt.qh) * (int64_t)D;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
             uint4 u = qvalid ? *(const uint4*)(qp + kb * 16 + h * 8) : make_uint4(0, 0, 0, 0);
@@ -71,40 +170,56 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(FwdParams p) {
     for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
-    float m_run = kNegInf, l_run = 0.f;
+    float m_run = kNegInf, l_run = 0.f, lr_run = 0.f;
+    const bf16x2 kOnes = {(__bf16)1.0f, (__bf16)1.0f};
 
     const int64_t row_stride = (int64_t)p.Hkv * D;
     const uint16_t* Kg = (const uint16_t*)p.K + ((int64_t)qt.b * p.S * p.Hkv + qt.kvh) * D;
     const uint16_t* Vg = (const uint16_t*)p.V + ((int64_t)qt.b * p.S * p.Hkv + qt.kvh) * D;
 
+    // ---- pipeline: tile i computed from LDS[i%2], tile i+1 staged in
+    // registers, tile i+2's loads issued during iteration i
     KvIter it;
-    bool have = kv_first(p, qt.rank, qmax, BN, it);
     typename T::Regs regs;
-    if (have) {
-        const int64_t r0 = it.krow + (int64_t)it.tile * BN;
-        const int64_t left = p.c - (int64_t)it.tile * BN;
-        T::load(regs, Kg + r0 * row_stride, Vg + r0 * row_stride, row_stride,
-                left < BN ? (int)left : BN, threadIdx.x);
-        T::store(regs, lds[0], lds[0] + T::ELEMS, threadIdx.x);
+    TileDesc dc, dr;
+    bool have_c = kv_first(p, qt.rank, qmax, BN, it);
+    bool have_r = false;
+    if (have_c) {
+        dc = tile_desc(p, it);
+        T::load(regs, Kg + dc.krow * row_stride, Vg + dc.krow * row_stride, row_stride, dc.klen, t);
+        T::store(regs, ldsK[0], ldsV[0], t);
+        have_r = kv_next(p, qt.rank, qmax, BN, it);
+        if (have_r) {
+            dr = tile_desc(p, it);
+            T::load(regs, Kg + dr.krow * row_stride, Vg + dr.krow * row_stride, row_stride, dr.klen, t);
+        }
     }
     __syncthreads();
 
+    // transpose-read addressing of the V operand: lane l of 16-lane group g
+    // points at row 8*(g>>1) + (l%16)/4 (+4 for the second read) and dims
+    // 16*(g&1) + 4*(l%4); it receives 4 consecutive keys of dim 16*(g&1)+l%16
+    const int tr_g = lane >> 4, tr_i = lane & 15;
+    const int tr_row = 8 * (tr_g >> 1) + (tr_i >> 2);
+    const int tr_col = 16 * (tr_g & 1) + 4 * (tr_i & 3);
+
     int buf = 0;
-    while (have) {
-        const int64_t kpos0 = it.kpos + (int64_t)it.tile * BN;
-        const int64_t kleft = p.c - (int64_t)it.tile * BN;
-        const int klen = kleft < BN ? (int)kleft : BN;
-        const bool nxt = kv_next(p, qt.rank, qmax, BN, it);
-        if (nxt) {
-            const int64_t r0 = it.krow + (int64_t)it.tile * BN;
-            const int64_t left = p.c - (int64_t)it.tile * BN;
-            T::load(regs, Kg + r0 * row_stride, Vg + r0 * row_stride, row_stride,
-                    left < BN ? (int)left : BN, threadIdx.x);
+    while (have_c) {
+        bool have_l = false;
+        TileDesc dl;
+        if (have_r) {
+            T::store(regs, ldsK[buf ^ 1], ldsV[buf ^ 1], t);
+            have_l = kv_next(p, qt.rank, qmax, BN, it);
+            if (have_l) {
+                dl = tile_desc(p, it);
+                T::load(regs, Kg + dl.krow * row_stride, Vg + dl.krow * row_stride, row_stride,
+                        dl.klen, t);
+            }
         }
 
-        const uint16_t* Ks = lds[buf];
-        const uint16_t* Vts = lds[buf] + T::ELEMS;
-        const bool active = wrows > 0 && !(p.causal && kpos0 > wq_hi);
+        const uint16_t* Ks = ldsK[buf];
+        const uint16_t* Vs = ldsV[buf];
+        const bool active = wrows > 0 && !(p.causal && dc.kpos > wq_hi);
         if (active) {
             // ---- S^T = K Q^T (64 keys x 32 queries)
             f32x16 sacc[2];
@@ -121,68 +236,86 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(FwdParams p) {
             }
             // ---- mask (diagonal / ragged tiles only); register r of block kb2
             // holds key kb2*32 + 16*(r/8) + 8h + (r%8)
-            const bool need_mask = klen < BN || (p.causal && kpos0 + BN - 1 > wq_lo);
+            const bool need_mask = dc.klen < BN || (p.causal && dc.kpos + BN - 1 > wq_lo);
             if (need_mask) {
 #pragma unroll
                 for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int kidx = kb2 * 32 + 16 * (r >> 3) + 8 * h + (r & 7);
-                        const bool ok = kidx < klen && (!p.causal || kpos0 + kidx <= qpos);
+                        const bool ok = kidx < dc.klen && (!p.causal || dc.kpos + kidx <= qpos);
                         if (!ok) sacc[kb2][r] = kNegInf;
                     }
             }
-            // ---- online softmax update
+            // ---- online softmax update with a lazily moved reference max
             float mx = kNegInf;
 #pragma unroll
             for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb2][r]);
-            mx = xor32_max(mx);
-            const float m_new = fmaxf(m_run, mx * p.scale_log2);
-            const float m_use = m_new == kNegInf ? 0.f : m_new;
-            const float alpha = fast_exp2(m_run - m_use);
+            mx = halves_max(mx) * p.scale_log2;
+            const bool move = mx > m_run + kLazy;
+            const float m_ref = move ? mx : m_run;
+            const float m_use = m_ref == kNegInf ? 0.f : m_ref;
+            if (__builtin_amdgcn_ballot_w64(move) != 0) {
+                const float alpha = fast_exp2(m_run - m_use);
+                l_run *= alpha;
+                lr_run *= alpha;
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+            }
+            m_run = m_ref;
+            // exponentials: l_run sums them exactly (for the LSE); lr_run sums
+            // the bf16-rounded values the PV product actually uses (for O),
+            // so a dominant key's rounding cancels in O = sum(p V) / sum(p)
             float lsum = 0.f;
-#pragma unroll
-            for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float e = fast_exp2(__builtin_fmaf(sacc[kb2][r], p.scale_log2, -m_use));
-                    sacc[kb2][r] = e;
-                    lsum += e;
-                }
-            l_run = l_run * alpha + lsum;
-            m_run = m_new;
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-            // ---- P^T as the B operand: 16-key block kk = registers 8*(kk%2).. of kb2 = kk/2
             bf16x8 pb[4];
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-                for (int i = 0; i < 8; ++i) pb[kk][i] = (__bf16)sacc[kk >> 1][8 * (kk & 1) + i];
-            // ---- O^T += V^T P^T
+                for (int i = 0; i < 8; i += 2) {
+                    const float e0 = fast_exp2(
+                        __builtin_fmaf(sacc[kk >> 1][8 * (kk & 1) + i], p.scale_log2, -m_use));
+                    const float e1 = fast_exp2(
+                        __builtin_fmaf(sacc[kk >> 1][8 * (kk & 1) + i + 1], p.scale_log2, -m_use));
+                    lsum += e0 + e1;
+                    bf16x2 pr;
+                    pr[0] = (__bf16)e0;
+                    pr[1] = (__bf16)e1;
+                    lr_run = __builtin_amdgcn_fdot2_f32_bf16(pr, kOnes, lr_run, false);
+                    pb[kk][i] = pr[0];
+                    pb[kk][i + 1] = pr[1];
+                }
+            l_run += lsum;
+            // ---- O^T += V^T P^T; P^T block kk holds keys 16kk + 8h + 0..7
 #pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                const int dim = db * 32 + m;
+            for (int kk = 0; kk < 4; ++kk) {
+                const int r0 = 16 * kk + tr_row;
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-                    const bf16x8 a = *(const bf16x8*)(Vts + T::vt_off(dim, 2 * kk + h));
+                for (int db = 0; db < DB; ++db) {
+                    const int col = db * 32 + tr_col;
+                    const i16x4 lo = ds_read_tr(Vs + T::v_off(r0, col >> 3) + (col & 7));
+                    const i16x4 hi = ds_read_tr(Vs + T::v_off(r0 + 4, col >> 3) + (col & 7));
+                    const bf16x8 a = __builtin_bit_cast(
+                        bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
                     oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kk], oacc[db], 0, 0, 0);
                 }
             }
         }
-        if (nxt) T::store(regs, lds[buf ^ 1], lds[buf ^ 1] + T::ELEMS, threadIdx.x);
         __syncthreads();
         buf ^= 1;
-        have = nxt;
+        dc = dr;
+        have_c = have_r;
+        dr = dl;
+        have_r = have_l;
     }
 
     // ---- finalize: O = O / l, LSE = m + ln l (natural log)
-    const float l_tot = xor32_sum(l_run);
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const float l_tot = halves_sum(l_run);
+    const float lr_tot = halves_sum(lr_run);
+    const float inv = lr_tot > 0.f ? 1.f / lr_tot : 0.f;
     if (qvalid) {
         const int64_t obase = ((qt.b * p.q_rows + qt.q_row0 + qi) * p.Hq + qt.qh) * (int64_t)D;
 #pragma unroll

@@ -72,7 +72,7 @@ hipError_t launch_layout(const void* src, void* dst, int64_t outer, int64_t S, i
                          int P, int zigzag, int inverse, hipStream_t s);
 
 // Tile shapes of the prefill kernels (the host needs them for the grid).
-constexpr int FWD_BF16_BLOCK_M = 128;
+constexpr int FWD_BF16_BLOCK_M = 256;
 constexpr int FWD_F32_BLOCK_M = 64;
 
 }  // namespace ra
