@@ -102,7 +102,9 @@ def main() -> int:
     ap.add_argument("--decode-parts", type=int, default=64)
     ap.add_argument("--cpu-rows", type=int, default=128)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", choices=["all", "prefill", "decode"], default="all")
+    ap.add_argument("--workload", choices=["all", "prefill", "decode", "copy"], default="all",
+                    help="copy: a plain 1 GiB device copy through the layout kernel (contiguous "
+                         "layout), used to calibrate the HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (--gpus {args.gpus} requested): the ring is "
@@ -123,6 +125,22 @@ def main() -> int:
     dev = torch.device("cuda:0")
     do_pre = args.workload in ("all", "prefill")
     do_dec = args.workload in ("all", "decode")
+    if args.workload == "copy":
+        nbytes = 1 << 30
+        src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup):
+            ra.ra_layout_gather(src, dst, 1 << 20, 1, "contiguous", inverse=False, outer=1)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            ra.ra_layout_gather(src, dst, 1 << 20, 1, "contiguous", inverse=False, outer=1)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        print(json.dumps({"workload": "copy", "bytes_read": nbytes, "bytes_written": nbytes,
+                          "ms": ms, "GB/s": 2 * nbytes / (ms * 1e-3) / 1e9}), flush=True)
+        return 0
     wp, wd = WORKLOADS[4], WORKLOADS[5]
 
     launches = []  # (stage, fn)
