@@ -29,10 +29,14 @@
 // key-major in LDS and the PV operand (8 consecutive keys of one dim per
 // lane) is read with the gfx950 transpose load ds_read_b64_tr_b16.
 //
-// K and V tiles are double-buffered in LDS.  Each thread stages 1/512 of the
-// next tile in registers: tile i+1 is written to LDS and tile i+2's global
-// loads are issued before the MFMAs of tile i, so their latency hides behind
-// a whole tile of compute; one barrier per tile.
+// Schedule.  The waves form two groups, 0-3 and 4-7, with one wave of each
+// on every SIMD.  An iteration has two phases separated by barriers: an MFMA
+// phase (O += V_{i-1} P_{i-1}, then S_i = K_i Q^T) and a VALU phase (softmax
+// of S_i, plus staging the next K/V rows).  Group 1 starts one phase late, so
+// on every SIMD one wave issues MFMAs while the other runs its exponentials.
+// K/V tiles live in a ring of three LDS buffers; each group stages half of
+// every tile through registers (tile i+1+group is written in the VALU phase of
+// iteration i, and its successor's global loads are issued right after).
 #include "ra_device.h"
 
 namespace ra {
@@ -41,6 +45,8 @@ namespace {
 constexpr int BM = FWD_BF16_BLOCK_M;  // queries per work-group (8 waves x 32)
 constexpr int BN = 64;                // keys per tile
 constexpr int NT = 512;               // threads per work-group
+constexpr int GT = 256;               // threads per wave group
+constexpr int NBUF = 3;               // LDS ring depth
 constexpr float kLazy = 8.0f;         // log2 headroom before the reference max moves
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -48,10 +54,11 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 template <int D>
 struct KvTile {
-    static constexpr int KCH = D / 8;              // 16-byte chunks per row
-    static constexpr int LOADS = BN * KCH / NT;    // 16-byte loads per thread per tensor
+    static constexpr int KCH = D / 8;                   // 16-byte chunks per row
+    static constexpr int HALF = BN / 2;                 // rows staged by one wave group
+    static constexpr int LOADS = HALF * KCH / GT;       // 16-byte loads per thread per tensor
     static constexpr int ELEMS = BN * D;
-    static_assert(LOADS >= 1 && BN * KCH % NT == 0, "tile split");
+    static_assert(LOADS >= 1 && HALF * KCH % GT == 0, "tile split");
 
     // K: chunk c of row r lives at chunk c ^ (r mod KCH): the 32 rows x 2
     // chunks of one MFMA operand read hit every bank equally.
@@ -72,24 +79,26 @@ struct KvTile {
         uint4 v[LOADS];
     };
 
-    // global -> registers; rows >= klen load as zero
+    // Rows [32*grp, 32*grp + 32) of a tile, global -> registers; rows at or
+    // beyond klen (the ragged end of a chunk) load as zero.
     static __device__ __forceinline__ void load(Regs& r, const uint16_t* Kb, const uint16_t* Vb,
-                                                int64_t row_stride, int klen, int t) {
+                                                int64_t row_stride, int klen, int grp, int gt) {
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) {
-            const int id = t + NT * i;
-            const int row = id / KCH, ch = id % KCH;
+            const int id = gt + GT * i;
+            const int row = HALF * grp + id / KCH, ch = id % KCH;
             const bool ok = row < klen;
             const int64_t off = row * row_stride + ch * 8;
             r.k[i] = ok ? *(const uint4*)(Kb + off) : make_uint4(0, 0, 0, 0);
             r.v[i] = ok ? *(const uint4*)(Vb + off) : make_uint4(0, 0, 0, 0);
         }
     }
-    static __device__ __forceinline__ void store(const Regs& r, uint16_t* Ks, uint16_t* Vs, int t) {
+    static __device__ __forceinline__ void store(const Regs& r, uint16_t* Ks, uint16_t* Vs, int grp,
+                                                 int gt) {
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) {
-            const int id = t + NT * i;
-            const int row = id / KCH, ch = id % KCH;
+            const int id = gt + GT * i;
+            const int row = HALF * grp + id / KCH, ch = id % KCH;
             *(uint4*)(Ks + k_off(row, ch)) = r.k[i];
             *(uint4*)(Vs + v_off(row, ch)) = r.v[i];
         }
@@ -137,13 +146,15 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdParams p) {
     using T = KvTile<D>;
     constexpr int KB = D / 16;  // MFMA k-blocks of Q K^T
     constexpr int DB = D / 32;  // 32-dim blocks of O^T
-    __shared__ __attribute__((aligned(16))) uint16_t ldsK[2][T::ELEMS];
-    __shared__ __attribute__((aligned(16))) uint16_t ldsV[2][T::ELEMS];
+    __shared__ __attribute__((aligned(16))) uint16_t ldsK[NBUF][T::ELEMS];
+    __shared__ __attribute__((aligned(16))) uint16_t ldsV[NBUF][T::ELEMS];
 
     const QTile qt = decode_qtile<BM>(p, blockIdx.x);
     const int t = threadIdx.x;
-    const int lane = t & 63, w = t >> 6;
+    const int lane = t & 63;
+    const int w = __builtin_amdgcn_readfirstlane(t >> 6);  // wave index, uniform in the wave
     const int h = lane >> 5, m = lane & 31;
+    const int grp = w >> 2, gt = t & (GT - 1);  // wave group; one wave of each per SIMD
 
     // this lane's query (MFMA column m of the wave's 32 queries)
     const int qi = w * 32 + m;
@@ -177,24 +188,27 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdParams p) {
     const uint16_t* Kg = (const uint16_t*)p.K + ((int64_t)qt.b * p.S * p.Hkv + qt.kvh) * D;
     const uint16_t* Vg = (const uint16_t*)p.V + ((int64_t)qt.b * p.S * p.Hkv + qt.kvh) * D;
 
-    // ---- pipeline: tile i computed from LDS[i%2], tile i+1 staged in
-    // registers, tile i+2's loads issued during iteration i
-    KvIter it;
+    // ---- prologue: tile 0 in LDS (both halves), group 1's half of tile 1 in
+    // LDS, and each group's next half-tile (1 + grp) in registers
+    const int n = kv_count(p, qt.rank, qmax, BN);
+    KvIter it_c, it_l;
     typename T::Regs regs;
-    TileDesc dc, dr;
-    bool have_c = kv_first(p, qt.rank, qmax, BN, it);
-    bool have_r = false;
-    if (have_c) {
-        dc = tile_desc(p, it);
-        T::load(regs, Kg + dc.krow * row_stride, Vg + dc.krow * row_stride, row_stride, dc.klen, t);
-        T::store(regs, ldsK[0], ldsV[0], t);
-        have_r = kv_next(p, qt.rank, qmax, BN, it);
-        if (have_r) {
-            dr = tile_desc(p, it);
-            T::load(regs, Kg + dr.krow * row_stride, Vg + dr.krow * row_stride, row_stride, dr.klen, t);
+    if (n > 0) {
+        kv_first(p, qt.rank, qmax, BN, it_c);
+        it_l = it_c;
+        TileDesc d0 = tile_desc(p, it_c);
+        T::load(regs, Kg + d0.krow * row_stride, Vg + d0.krow * row_stride, row_stride, d0.klen, grp, gt);
+        T::store(regs, ldsK[0], ldsV[0], grp, gt);
+        for (int j = 1; j <= 1 + grp && j < n; ++j) {
+            kv_next(p, qt.rank, qmax, BN, it_l);
+            const TileDesc dj = tile_desc(p, it_l);
+            T::load(regs, Kg + dj.krow * row_stride, Vg + dj.krow * row_stride, row_stride, dj.klen,
+                    grp, gt);
+            if (j < 1 + grp) T::store(regs, ldsK[j], ldsV[j], grp, gt);
         }
     }
     __syncthreads();
+    if (grp == 1) __syncthreads();  // group 1 runs one phase behind group 0
 
     // transpose-read addressing of the V operand: lane l of 16-lane group g
     // points at row 8*(g>>1) + (l%16)/4 (+4 for the second read) and dims
@@ -203,26 +217,36 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdParams p) {
     const int tr_row = 8 * (tr_g >> 1) + (tr_i >> 2);
     const int tr_col = 16 * (tr_g & 1) + 4 * (tr_i & 3);
 
-    int buf = 0;
-    while (have_c) {
-        bool have_l = false;
-        TileDesc dl;
-        if (have_r) {
-            T::store(regs, ldsK[buf ^ 1], ldsV[buf ^ 1], t);
-            have_l = kv_next(p, qt.rank, qmax, BN, it);
-            if (have_l) {
-                dl = tile_desc(p, it);
-                T::load(regs, Kg + dl.krow * row_stride, Vg + dl.krow * row_stride, row_stride,
-                        dl.klen, t);
+    bf16x8 pb[4];
+    bool act_prev = false;
+
+    // O += V_j P_j^T for the tile in LDS buffer `buf` (keys 16kk + 8h + 0..7
+    // of P^T block kk)
+    auto pv = [&](int buf) {
+        const uint16_t* Vs = ldsV[buf];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const int r0 = 16 * kk + tr_row;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const int col = db * 32 + tr_col;
+                const i16x4 lo = ds_read_tr(Vs + T::v_off(r0, col >> 3) + (col & 7));
+                const i16x4 hi = ds_read_tr(Vs + T::v_off(r0 + 4, col >> 3) + (col & 7));
+                const bf16x8 a = __builtin_bit_cast(
+                    bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kk], oacc[db], 0, 0, 0);
             }
         }
+    };
 
-        const uint16_t* Ks = ldsK[buf];
-        const uint16_t* Vs = ldsV[buf];
-        const bool active = wrows > 0 && !(p.causal && dc.kpos > wq_hi);
-        if (active) {
-            // ---- S^T = K Q^T (64 keys x 32 queries)
-            f32x16 sacc[2];
+    for (int i = 0; i < n; ++i) {
+        // ================= MFMA phase: O += V_{i-1} P_{i-1}; S_i = K_i Q^T
+        const TileDesc dc = tile_desc(p, it_c);
+        const bool act = wrows > 0 && !(p.causal && dc.kpos > wq_hi);
+        if (act_prev) pv((i + NBUF - 1) % NBUF);
+        f32x16 sacc[2];
+        if (act) {
+            const uint16_t* Ks = ldsK[i % NBUF];
 #pragma unroll
             for (int kb2 = 0; kb2 < 2; ++kb2) {
 #pragma unroll
@@ -234,20 +258,29 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdParams p) {
                     sacc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[kb], sacc[kb2], 0, 0, 0);
                 }
             }
-            // ---- mask (diagonal / ragged tiles only); register r of block kb2
-            // holds key kb2*32 + 16*(r/8) + 8h + (r%8)
+        }
+        __syncthreads();
+
+        // ================= VALU phase: softmax of S_i; stage K/V rows
+        if (act) {
+            // mask (diagonal / ragged tiles only): register r of block kb2
+            // holds key kb2*32 + 16*(r/8) + 8h + (r%8); keys >= lim are masked
             const bool need_mask = dc.klen < BN || (p.causal && dc.kpos + BN - 1 > wq_lo);
             if (need_mask) {
+                int lim = dc.klen;
+                if (p.causal) {
+                    const int64_t vis = qpos - dc.kpos + 1;
+                    lim = vis < (int64_t)lim ? (vis < 0 ? 0 : (int)vis) : lim;
+                }
+                lim -= 8 * h;
 #pragma unroll
                 for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        const int kidx = kb2 * 32 + 16 * (r >> 3) + 8 * h + (r & 7);
-                        const bool ok = kidx < dc.klen && (!p.causal || dc.kpos + kidx <= qpos);
-                        if (!ok) sacc[kb2][r] = kNegInf;
+                        const int k0 = kb2 * 32 + 16 * (r >> 3) + (r & 7);
+                        sacc[kb2][r] = k0 < lim ? sacc[kb2][r] : kNegInf;
                     }
             }
-            // ---- online softmax update with a lazily moved reference max
             float mx = kNegInf;
 #pragma unroll
             for (int kb2 = 0; kb2 < 2; ++kb2)
@@ -267,50 +300,47 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdParams p) {
                     for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
             }
             m_run = m_ref;
-            // exponentials: l_run sums them exactly (for the LSE); lr_run sums
-            // the bf16-rounded values the PV product actually uses (for O),
-            // so a dominant key's rounding cancels in O = sum(p V) / sum(p)
+            // l_run sums the exponentials exactly (for the LSE); lr_run sums
+            // the bf16-rounded values the PV product uses (for O), so a
+            // dominant key's rounding cancels in O = sum(p V) / sum(p)
             float lsum = 0.f;
-            bf16x8 pb[4];
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-                for (int i = 0; i < 8; i += 2) {
+                for (int i2 = 0; i2 < 8; i2 += 2) {
                     const float e0 = fast_exp2(
-                        __builtin_fmaf(sacc[kk >> 1][8 * (kk & 1) + i], p.scale_log2, -m_use));
+                        __builtin_fmaf(sacc[kk >> 1][8 * (kk & 1) + i2], p.scale_log2, -m_use));
                     const float e1 = fast_exp2(
-                        __builtin_fmaf(sacc[kk >> 1][8 * (kk & 1) + i + 1], p.scale_log2, -m_use));
+                        __builtin_fmaf(sacc[kk >> 1][8 * (kk & 1) + i2 + 1], p.scale_log2, -m_use));
                     lsum += e0 + e1;
                     bf16x2 pr;
                     pr[0] = (__bf16)e0;
                     pr[1] = (__bf16)e1;
                     lr_run = __builtin_amdgcn_fdot2_f32_bf16(pr, kOnes, lr_run, false);
-                    pb[kk][i] = pr[0];
-                    pb[kk][i + 1] = pr[1];
+                    pb[kk][i2] = pr[0];
+                    pb[kk][i2 + 1] = pr[1];
                 }
             l_run += lsum;
-            // ---- O^T += V^T P^T; P^T block kk holds keys 16kk + 8h + 0..7
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const int r0 = 16 * kk + tr_row;
-#pragma unroll
-                for (int db = 0; db < DB; ++db) {
-                    const int col = db * 32 + tr_col;
-                    const i16x4 lo = ds_read_tr(Vs + T::v_off(r0, col >> 3) + (col & 7));
-                    const i16x4 hi = ds_read_tr(Vs + T::v_off(r0 + 4, col >> 3) + (col & 7));
-                    const bf16x8 a = __builtin_bit_cast(
-                        bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kk], oacc[db], 0, 0, 0);
-                }
+        }
+        // this group's half of tile i+1+grp -> LDS; then the next half-tile's loads
+        const int wi = i + 1 + grp;
+        if (wi < n) {
+            T::store(regs, ldsK[wi % NBUF], ldsV[wi % NBUF], grp, gt);
+            if (wi + 1 < n) {
+                kv_next(p, qt.rank, qmax, BN, it_l);
+                const TileDesc dl = tile_desc(p, it_l);
+                T::load(regs, Kg + dl.krow * row_stride, Vg + dl.krow * row_stride, row_stride,
+                        dl.klen, grp, gt);
             }
         }
         __syncthreads();
-        buf ^= 1;
-        dc = dr;
-        have_c = have_r;
-        dr = dl;
-        have_r = have_l;
+        act_prev = act;
+        if (i + 1 < n) kv_next(p, qt.rank, qmax, BN, it_c);
     }
+    // last MFMA phase: O += V_{n-1} P_{n-1}
+    if (act_prev) pv((n + NBUF - 1) % NBUF);
+    __syncthreads();
+    if (grp == 0) __syncthreads();  // matches group 1's extra barrier
 
     // ---- finalize: O = O / l, LSE = m + ln l (natural log)
     const float l_tot = halves_sum(l_run);

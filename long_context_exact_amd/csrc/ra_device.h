@@ -138,6 +138,18 @@ __device__ __forceinline__ bool kv_first(const FwdParams& p, int rank, int64_t q
     return true;
 }
 
+// Number of key tiles the iteration visits.
+__device__ __forceinline__ int kv_count(const FwdParams& p, int rank, int64_t qmax, int bn) {
+    KvIter it;
+    int n = 0;
+    for (it.t = 0; it.t < p.P; ++it.t)
+        for (it.lc = 0; it.lc < p.chunks_per_rank; ++it.lc) {
+            kv_seg(p, rank, qmax, bn, it);
+            n += it.ntiles;
+        }
+    return n;
+}
+
 __device__ __forceinline__ bool kv_next(const FwdParams& p, int rank, int64_t qmax, int bn,
                                         KvIter& it) {
     ++it.tile;
