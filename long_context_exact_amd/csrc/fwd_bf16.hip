@@ -25,9 +25,12 @@
 // along columns) so each lane holds whole rows of its own query.  The K rows
 // fed to the first MFMA are permuted (bits 2 and 3 of the row index swapped)
 // so the accumulator hands every lane 8 consecutive keys per 16-key block:
-// exactly the B operand of the second MFMA, with no data movement.  V stays
-// key-major in LDS and the PV operand (8 consecutive keys of one dim per
-// lane) is read with the gfx950 transpose load ds_read_b64_tr_b16.
+// exactly the B operand of the second MFMA, with no data movement.  V is
+// stored transposed in LDS (V^T: keys contiguous, one row per head dim), so
+// the PV operand (8 consecutive keys of one dim per lane) is one 16-byte LDS
+// read, like the K operand.  The transpose is done in registers while the
+// tile is staged, in the VALU phase; transposing LDS reads in the MFMA phase
+// would cost it about three times the LDS issue time per operand.
 //
 // Schedule.  The waves form two groups, 0-3 and 4-7, with one wave of each
 // on every SIMD.  An iteration has two phases separated by barriers: an MFMA
@@ -49,15 +52,26 @@ constexpr int GT = 256;               // threads per wave group
 constexpr int NBUF = 3;               // LDS ring depth
 constexpr float kLazy = 8.0f;         // log2 headroom before the reference max moves
 
-typedef short i16x4 __attribute__((ext_vector_type(4)));
+#ifndef RA_FWD_VT
+#define RA_FWD_VT 0       // 1: V transposed in LDS (16-byte PV reads); 0: row-major V, transpose reads
+#endif
+#ifndef RA_FWD_PIN
+#define RA_FWD_PIN 1      // pin the MFMA / operand-read interleave
+#endif
+#ifndef RA_FWD_AHEAD
+#define RA_FWD_AHEAD 4    // MFMA operands read ahead of use in the MFMA phase
+#endif
+
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 template <int D>
-struct KvTile {
+struct KvTileRow {
     static constexpr int KCH = D / 8;                   // 16-byte chunks per row
     static constexpr int HALF = BN / 2;                 // rows staged by one wave group
     static constexpr int LOADS = HALF * KCH / GT;       // 16-byte loads per thread per tensor
     static constexpr int ELEMS = BN * D;
+    static constexpr int K_ELEMS = ELEMS, V_ELEMS = ELEMS;
     static_assert(LOADS >= 1 && HALF * KCH % GT == 0, "tile split");
 
     // K: chunk c of row r lives at chunk c ^ (r mod KCH): the 32 rows x 2
@@ -105,6 +119,100 @@ struct KvTile {
     }
 };
 
+// V stored transposed (V^T) with 256-byte rows, for 16-byte PV operand reads.
+template <int D>
+struct KvTileVt {
+    static constexpr int KCH = D / 8;                   // 16-byte chunks per K row
+    static constexpr int HALF = BN / 2;                 // keys staged by one wave group
+    static constexpr int K_LOADS = HALF * KCH / GT;     // 16-byte K loads per thread
+    static constexpr int V_UNITS = (HALF / 2) * KCH;    // (2 keys x 8 dims) V units per half tile
+    static constexpr int K_ELEMS = BN * D;
+    static constexpr int VT_STRIDE = 2 * BN;            // V^T row pitch in elements (256 bytes)
+    static constexpr int V_ELEMS = D * VT_STRIDE;
+    static_assert(K_LOADS >= 1 && K_LOADS <= 2 && HALF * KCH % GT == 0 && V_UNITS <= GT, "tile split");
+
+    // K, row-major: chunk c of row r lives at chunk c ^ (r mod KCH); the 32
+    // rows x 2 chunks of one MFMA operand read hit every bank equally.
+    static __device__ __forceinline__ int k_off(int row, int ch) {
+        return row * D + ((ch ^ (row & (KCH - 1))) << 3);
+    }
+    // V^T: one row per head dimension, BN keys used out of a 256-byte pitch;
+    // 8-key chunk c of row d lives at chunk c ^ (d mod 16) ^ ((d >> 4) mod 8).
+    // Measured with the LDS bank-conflict counter, the PV operand read (32
+    // consecutive dims x 2 chunks) is conflict-free; the staging writes below
+    // (4 bytes = 2 keys of one dim, dims 8c+j of the 16 chunks c) cover 64
+    // distinct banks.  With the (d mod 16) term alone 8-byte transposed
+    // writes conflict 16-way.
+    static __device__ __forceinline__ int vt_off(int dim, int ch) {
+        return dim * VT_STRIDE + ((ch ^ (dim & 15) ^ ((dim >> 4) & 7)) << 3);
+    }
+
+    // Staging of one wave group's half tile (keys 32*grp .. 32*grp+31).  Every
+    // thread carries K_LOADS 16-byte chunks of K and one unit of V: 2
+    // consecutive keys x 8 dims, transposed in registers on the way to LDS.
+    struct Regs {
+        uint4 k0, k1, v0, v1;
+    };
+
+    static __device__ __forceinline__ void load(Regs& r, const uint16_t* Kb, const uint16_t* Vb,
+                                                int64_t row_stride, int klen, int grp, int gt) {
+        {
+            const int row = HALF * grp + gt / KCH, ch = gt % KCH;
+            r.k0 = row < klen ? *(const uint4*)(Kb + row * row_stride + ch * 8) : make_uint4(0, 0, 0, 0);
+        }
+        if (K_LOADS > 1) {
+            const int id = gt + GT;
+            const int row = HALF * grp + id / KCH, ch = id % KCH;
+            r.k1 = row < klen ? *(const uint4*)(Kb + row * row_stride + ch * 8) : make_uint4(0, 0, 0, 0);
+        }
+        if (gt < V_UNITS) {
+            const int ch = gt % KCH, kp = gt / KCH;
+            const int row = HALF * grp + 2 * kp;
+            r.v0 = row < klen ? *(const uint4*)(Vb + row * row_stride + ch * 8) : make_uint4(0, 0, 0, 0);
+            r.v1 = row + 1 < klen ? *(const uint4*)(Vb + (row + 1) * row_stride + ch * 8)
+                                  : make_uint4(0, 0, 0, 0);
+        }
+    }
+
+    static __device__ __forceinline__ void store(const Regs& r, uint16_t* Ks, uint16_t* Vts, int grp,
+                                                 int gt) {
+        {
+            const int row = HALF * grp + gt / KCH, ch = gt % KCH;
+            *(uint4*)(Ks + k_off(row, ch)) = r.k0;
+        }
+        if (K_LOADS > 1) {
+            const int id = gt + GT;
+            const int row = HALF * grp + id / KCH, ch = id % KCH;
+            *(uint4*)(Ks + k_off(row, ch)) = r.k1;
+        }
+        if (gt < V_UNITS) {
+            const int ch = gt % KCH, kp = gt / KCH;
+            const int key0 = HALF * grp + 2 * kp;  // keys key0, key0+1; dims 8ch..8ch+7
+            const uint32_t a[4] = {r.v0.x, r.v0.y, r.v0.z, r.v0.w};
+            const uint32_t b[4] = {r.v1.x, r.v1.y, r.v1.z, r.v1.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                // dword j of a key row holds dims 2j (low half) and 2j+1 (high half)
+                const int d0 = 8 * ch + 2 * j;
+                *(uint32_t*)(Vts + vt_off(d0, key0 >> 3) + (key0 & 7)) =
+                    __builtin_amdgcn_perm(b[j], a[j], 0x05040100u);
+                *(uint32_t*)(Vts + vt_off(d0 + 1, key0 >> 3) + (key0 & 7)) =
+                    __builtin_amdgcn_perm(b[j], a[j], 0x07060302u);
+            }
+        }
+    }
+};
+
+#if RA_FWD_VT
+template <int D> using KvTile = KvTileVt<D>;
+#else
+template <int D> using KvTile = KvTileRow<D>;
+#endif
+
+__device__ __forceinline__ i16x4 ds_read_tr(const uint16_t* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
+}
+
 __device__ __forceinline__ int swap_bits23(int m) {
     return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
 }
@@ -119,10 +227,6 @@ __device__ __forceinline__ float halves_sum(float x) {
     const unsigned u = __builtin_bit_cast(unsigned, x);
     const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
     return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
-}
-
-__device__ __forceinline__ i16x4 ds_read_tr(const uint16_t* p) {
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
 }
 
 struct TileDesc {
@@ -146,8 +250,8 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdParams p) {
     using T = KvTile<D>;
     constexpr int KB = D / 16;  // MFMA k-blocks of Q K^T
     constexpr int DB = D / 32;  // 32-dim blocks of O^T
-    __shared__ __attribute__((aligned(16))) uint16_t ldsK[NBUF][T::ELEMS];
-    __shared__ __attribute__((aligned(16))) uint16_t ldsV[NBUF][T::ELEMS];
+    __shared__ __attribute__((aligned(16))) uint16_t ldsK[NBUF][T::K_ELEMS];
+    __shared__ __attribute__((aligned(16))) uint16_t ldsV[NBUF][T::V_ELEMS];  // V^T, padded rows
 
     const QTile qt = decode_qtile<BM>(p, blockIdx.x);
     const int t = threadIdx.x;
@@ -207,62 +311,96 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdParams p) {
             if (j < 1 + grp) T::store(regs, ldsK[j], ldsV[j], grp, gt);
         }
     }
+    // the first MFMA phase multiplies P = 0 by the V buffer "before" tile 0:
+    // zero it so no stale bits (NaN patterns) reach the accumulators
+    for (int e = t * 8; e < T::V_ELEMS; e += NT * 8)
+        *(uint4*)(&ldsV[NBUF - 1][e]) = make_uint4(0, 0, 0, 0);
+    // Drain the prologue's loads here: otherwise the wait-count analysis merges
+    // them into the loop header and makes the loop wait on in-flight staging
+    // loads at its first MFMA.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
     if (grp == 1) __syncthreads();  // group 1 runs one phase behind group 0
 
-    // transpose-read addressing of the V operand: lane l of 16-lane group g
-    // points at row 8*(g>>1) + (l%16)/4 (+4 for the second read) and dims
-    // 16*(g&1) + 4*(l%4); it receives 4 consecutive keys of dim 16*(g&1)+l%16
-    const int tr_g = lane >> 4, tr_i = lane & 15;
-    const int tr_row = 8 * (tr_g >> 1) + (tr_i >> 2);
-    const int tr_col = 16 * (tr_g & 1) + 4 * (tr_i & 3);
-
+    // P of the previous tile (zero before the first tile, whose "previous" V
+    // buffer is zeroed in the prologue, so the first PV product adds 0)
     bf16x8 pb[4];
-    bool act_prev = false;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int i2 = 0; i2 < 8; ++i2) pb[kk][i2] = (__bf16)0.f;
 
-    // O += V_j P_j^T for the tile in LDS buffer `buf` (keys 16kk + 8h + 0..7
-    // of P^T block kk)
-    auto pv = [&](int buf) {
-        const uint16_t* Vs = ldsV[buf];
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const int r0 = 16 * kk + tr_row;
-#pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                const int col = db * 32 + tr_col;
-                const i16x4 lo = ds_read_tr(Vs + T::v_off(r0, col >> 3) + (col & 7));
-                const i16x4 hi = ds_read_tr(Vs + T::v_off(r0 + 4, col >> 3) + (col & 7));
-                const bf16x8 a = __builtin_bit_cast(
-                    bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kk], oacc[db], 0, 0, 0);
-            }
+    // MFMA phase operands, in issue order: NPV blocks of O^T += V^T P^T (block
+    // j: keys 16*(j/DB).., dims 32*(j%DB)..), then NQK blocks of S^T = K Q^T
+    // (block j: keys 32*(j/KB).., dims 16*(j%KB)..).  Each operand is one
+    // 16-byte LDS read.
+    constexpr int NPV = 4 * DB, NQK = 2 * KB, NMF = NPV + NQK;
+    auto read_op = [&](int j, int buf) -> bf16x8 {
+        if (j < NPV) {
+            const int kk = j / DB, db = j % DB;
+#if RA_FWD_VT
+            return *(const bf16x8*)(ldsV[(buf + NBUF - 1) % NBUF] + T::vt_off(db * 32 + m, 2 * kk + h));
+#else
+            // transpose reads: lane l of 16-lane group g points at row
+            // 8*(g>>1) + (l%16)/4 (+4 for the second read) and dims
+            // 16*(g&1) + 4*(l%4); it receives 4 consecutive keys of one dim
+            const uint16_t* Vs = ldsV[(buf + NBUF - 1) % NBUF];
+            const int r0 = 16 * kk + 8 * (lane >> 5) + ((lane & 15) >> 2);
+            const int col = db * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+            const i16x4 lo = ds_read_tr(Vs + T::v_off(r0, col >> 3) + (col & 7));
+            const i16x4 hi = ds_read_tr(Vs + T::v_off(r0 + 4, col >> 3) + (col & 7));
+            return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#endif
         }
+        const int q = j - NPV, kb2 = q / KB, kb = q % KB;
+        const int row = kb2 * 32 + swap_bits23(m);
+        return *(const bf16x8*)(ldsK[buf] + T::k_off(row, kb * 2 + h));
     };
 
+    constexpr int AHEAD = RA_FWD_AHEAD;  // operands read ahead of their MFMA
     for (int i = 0; i < n; ++i) {
         // ================= MFMA phase: O += V_{i-1} P_{i-1}; S_i = K_i Q^T
+        // One straight-line block: every wave runs both products on every
+        // tile (a tile wholly in the future of a wave's queries is masked to
+        // P = 0 in the VALU phase), so the operand reads can be issued AHEAD
+        // MFMAs early and their LDS latency hides behind the matrix pipe.
         const TileDesc dc = tile_desc(p, it_c);
-        const bool act = wrows > 0 && !(p.causal && dc.kpos > wq_hi);
-        if (act_prev) pv((i + NBUF - 1) % NBUF);
+        const int cb = i % NBUF;
         f32x16 sacc[2];
-        if (act) {
-            const uint16_t* Ks = ldsK[i % NBUF];
 #pragma unroll
-            for (int kb2 = 0; kb2 < 2; ++kb2) {
+        for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) sacc[kb2][r] = 0.f;
-                const int row = kb2 * 32 + swap_bits23(m);
+            for (int r = 0; r < 16; ++r) sacc[kb2][r] = 0.f;
+        bf16x8 ops[AHEAD];
 #pragma unroll
-                for (int kb = 0; kb < KB; ++kb) {
-                    const bf16x8 a = *(const bf16x8*)(Ks + T::k_off(row, kb * 2 + h));
-                    sacc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[kb], sacc[kb2], 0, 0, 0);
-                }
+        for (int j = 0; j < AHEAD; ++j) ops[j] = read_op(j, cb);
+#if RA_FWD_PIN
+        // pin the issue order: the first AHEAD operands' reads, then per MFMA
+        // the read of the operand AHEAD positions later
+        __builtin_amdgcn_sched_group_barrier(0x100, RA_FWD_VT ? AHEAD : 2 * AHEAD, 0);
+#endif
+#pragma unroll
+        for (int j = 0; j < NMF; ++j) {
+            const bf16x8 a = ops[j % AHEAD];
+            if (j + AHEAD < NMF) ops[j % AHEAD] = read_op(j + AHEAD, cb);
+            if (j < NPV) {
+                oacc[j % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[j / DB], oacc[j % DB], 0, 0, 0);
+            } else {
+                const int q = j - NPV;
+                sacc[q / KB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[q % KB], sacc[q / KB], 0, 0, 0);
             }
+#if RA_FWD_PIN
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (!RA_FWD_VT && j + AHEAD < NPV)
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            else if (j + AHEAD < NMF)
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#endif
         }
         __syncthreads();
 
         // ================= VALU phase: softmax of S_i; stage K/V rows
-        if (act) {
+        {
             // mask (diagonal / ragged tiles only): register r of block kb2
             // holds key kb2*32 + 16*(r/8) + 8h + (r%8); keys >= lim are masked
             const bool need_mask = dc.klen < BN || (p.causal && dc.kpos + BN - 1 > wq_lo);
@@ -334,11 +472,14 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdParams p) {
             }
         }
         __syncthreads();
-        act_prev = act;
         if (i + 1 < n) kv_next(p, qt.rank, qmax, BN, it_c);
     }
     // last MFMA phase: O += V_{n-1} P_{n-1}
-    if (act_prev) pv((n + NBUF - 1) % NBUF);
+#pragma unroll
+    for (int j = 0; j < NPV; ++j) {
+        const bf16x8 a = read_op(j, n % NBUF);
+        oacc[j % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[j / DB], oacc[j % DB], 0, 0, 0);
+    }
     __syncthreads();
     if (grp == 0) __syncthreads();  // matches group 1's extra barrier
 
