@@ -9,37 +9,37 @@
 //   S^T = K Q^T          v_mfma_f32_32x32x16_bf16, fp32 accumulate
 //   mask                 only on tiles that cross the causal diagonal or the
 //                        ragged end of a chunk
-//   m~ = max(m, max S)   in-lane max over the lane's 32 scores + one
-//                        permlane32 swap (each lane owns one query)
-//   P = exp2(S*c - m')   c = log2(e)/sqrt(d) folded into one FMA
-//   l = l*a + sum P      lane-partial sums, a = exp2(m - m'); a second sum
-//                        of the bf16-rounded P (v_dot2 with ones) normalises O
+//   P = exp2(S*c - m')   c = log2(e)/sqrt(d) folded into one FMA; m' is the
+//                        lane's reference point (below)
+//   l = l*a + sum P      lane-partial sums; a second sum of the bf16-rounded P
+//                        (v_dot2 with ones) normalises O
 //   O^T = O^T*a + V^T P^T   v_mfma_f32_32x32x16_bf16 with P rounded to bf16
 //
-// The reference point m' of the exponentials is moved only when the running
-// maximum has grown by more than 2^8 since the last move (then P <= 256):
-// O and l are always taken relative to the same m', so the result is the
-// same; the 64 multiplies of the O rescale are skipped on most tiles.
+// Reference point.  O and l are kept relative to a reference m' that only
+// has to keep the exponentials in range, not equal the running maximum: a
+// tile whose 32 exponentials (per lane) sum to at most 2^8 is accepted as it
+// is, so most tiles need no max reduction and no O rescale.  Otherwise (and
+// until a lane has seen a finite score) the slow path takes the true maximum,
+// rescales l and O by a = exp2(m' - m'') and recomputes the tile's P.
 //
 // The score matrix is produced transposed (keys along MFMA rows, queries
 // along columns) so each lane holds whole rows of its own query.  The K rows
 // fed to the first MFMA are permuted (bits 2 and 3 of the row index swapped)
 // so the accumulator hands every lane 8 consecutive keys per 16-key block:
-// exactly the B operand of the second MFMA, with no data movement.  V is
-// stored transposed in LDS (V^T: keys contiguous, one row per head dim), so
-// the PV operand (8 consecutive keys of one dim per lane) is one 16-byte LDS
-// read, like the K operand.  The transpose is done in registers while the
-// tile is staged, in the VALU phase; transposing LDS reads in the MFMA phase
-// would cost it about three times the LDS issue time per operand.
+// exactly the B operand of the second MFMA, with no data movement.  V stays
+// row-major in LDS; its A operand (8 consecutive keys of one head dim per
+// lane) comes from two ds_read_b64_tr_b16 transposing reads.
 //
-// Schedule.  The waves form two groups, 0-3 and 4-7, with one wave of each
-// on every SIMD.  An iteration has two phases separated by barriers: an MFMA
-// phase (O += V_{i-1} P_{i-1}, then S_i = K_i Q^T) and a VALU phase (softmax
-// of S_i, plus staging the next K/V rows).  Group 1 starts one phase late, so
-// on every SIMD one wave issues MFMAs while the other runs its exponentials.
-// K/V tiles live in a ring of three LDS buffers; each group stages half of
-// every tile through registers (tile i+1+group is written in the VALU phase of
-// iteration i, and its successor's global loads are issued right after).
+// Schedule.  A wave issues independent VALU work behind its own MFMAs almost
+// for free, so every wave software-pipelines its own loop: in iteration i it
+// issues the MFMAs of S_{i+1} = K_{i+1} Q^T and O += V_{i-1} P_{i-1} and, in
+// between them, the softmax of S_i.  K/V tiles go from global memory straight
+// into a ring of four LDS buffers (global_load_lds_dwordx4, no staging
+// registers), two tiles ahead of the tile whose scores are being formed.  The
+// loop body is unrolled over the ring so that every LDS operand address is a
+// per-lane base plus an immediate offset.
+#include <type_traits>
+
 #include "ra_device.h"
 
 namespace ra {
@@ -47,167 +47,112 @@ namespace {
 
 constexpr int BM = FWD_BF16_BLOCK_M;  // queries per work-group (8 waves x 32)
 constexpr int BN = 64;                // keys per tile
-constexpr int NT = 512;               // threads per work-group
-constexpr int GT = 256;               // threads per wave group
-constexpr int NBUF = 3;               // LDS ring depth
-constexpr float kLazy = 8.0f;         // log2 headroom before the reference max moves
+constexpr int NW = 8;                 // waves per work-group
+constexpr int NT = 64 * NW;           // threads per work-group
+constexpr int NBUF = 4;               // LDS ring depth (K and V rings stay below 64 KB each)
+constexpr float kSumCap = 256.f;      // largest accepted per-lane tile sum of P
+static_assert(BM == 32 * NW, "32 queries per wave");
 
-#ifndef RA_FWD_VT
-#define RA_FWD_VT 0       // 1: V transposed in LDS (16-byte PV reads); 0: row-major V, transpose reads
-#endif
-#ifndef RA_FWD_PIN
-#define RA_FWD_PIN 1      // pin the MFMA / operand-read interleave
-#endif
 #ifndef RA_FWD_AHEAD
-#define RA_FWD_AHEAD 4    // MFMA operands read ahead of use in the MFMA phase
+#define RA_FWD_AHEAD 3    // LDS operands read ahead of their MFMAs
 #endif
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
+// 16 bytes per lane from global memory (uniform base + per-lane byte offset)
+// into LDS at lds_base + 16 * lane (lds_base in M0, uniform over the wave).
+// Written out so that the compiler's wait-count analysis, which cannot tell
+// the ring buffers apart, does not stall every LDS read on the loads in
+// flight; the kernel waits for them itself (vmcnt) before the barrier that
+// publishes a tile.  M0 is restored afterwards.
+__device__ __forceinline__ void lds_dma16(const void* base, uint32_t off, uint32_t lds_base) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %2\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(off), "s"(base), "s"(lds_base)
+        : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+}
+
+// K/V tile of BN rows x D dims, row-major in LDS with 16-byte chunk swizzles.
 template <int D>
-struct KvTileRow {
-    static constexpr int KCH = D / 8;                   // 16-byte chunks per row
-    static constexpr int HALF = BN / 2;                 // rows staged by one wave group
-    static constexpr int LOADS = HALF * KCH / GT;       // 16-byte loads per thread per tensor
+struct KvTile {
+    static constexpr int KCH = D / 8;               // 16-byte chunks per row
     static constexpr int ELEMS = BN * D;
-    static constexpr int K_ELEMS = ELEMS, V_ELEMS = ELEMS;
-    static_assert(LOADS >= 1 && HALF * KCH % GT == 0, "tile split");
+    static constexpr int ROUNDS = BN * KCH / NT;    // 16-byte loads per thread per tensor
+    static constexpr int LOADS = 2 * ROUNDS;        // loads per thread per tile
+    static_assert(ROUNDS >= 1 && BN * KCH % NT == 0, "tile split");
 
     // K: chunk c of row r lives at chunk c ^ (r mod KCH): the 32 rows x 2
     // chunks of one MFMA operand read hit every bank equally.
-    static __device__ __forceinline__ int k_off(int row, int ch) {
-        return row * D + ((ch ^ (row & (KCH - 1))) << 3);
-    }
-    // V: chunk c of row r lives at chunk c ^ s(r); one transpose read touches
-    // 8 rows (two groups of 4 consecutive) x 32 dims, spread over all banks.
-    static __device__ __forceinline__ int v_sw(int row) {
+    static __device__ __forceinline__ int k_swz(int row) { return row & (KCH - 1); }
+    // V: one transpose read touches 8 rows (two groups of 4 consecutive) x 32
+    // dims; the row-dependent chunk swizzle spreads them over all banks.
+    static __device__ __forceinline__ int v_swz(int row) {
         return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
     }
-    static __device__ __forceinline__ int v_off(int row, int ch) {
-        return row * D + ((ch ^ v_sw(row)) << 3);
-    }
-
-    struct Regs {
-        uint4 k[LOADS];
-        uint4 v[LOADS];
-    };
-
-    // Rows [32*grp, 32*grp + 32) of a tile, global -> registers; rows at or
-    // beyond klen (the ragged end of a chunk) load as zero.
-    static __device__ __forceinline__ void load(Regs& r, const uint16_t* Kb, const uint16_t* Vb,
-                                                int64_t row_stride, int klen, int grp, int gt) {
-#pragma unroll
-        for (int i = 0; i < LOADS; ++i) {
-            const int id = gt + GT * i;
-            const int row = HALF * grp + id / KCH, ch = id % KCH;
-            const bool ok = row < klen;
-            const int64_t off = row * row_stride + ch * 8;
-            r.k[i] = ok ? *(const uint4*)(Kb + off) : make_uint4(0, 0, 0, 0);
-            r.v[i] = ok ? *(const uint4*)(Vb + off) : make_uint4(0, 0, 0, 0);
-        }
-    }
-    static __device__ __forceinline__ void store(const Regs& r, uint16_t* Ks, uint16_t* Vs, int grp,
-                                                 int gt) {
-#pragma unroll
-        for (int i = 0; i < LOADS; ++i) {
-            const int id = gt + GT * i;
-            const int row = HALF * grp + id / KCH, ch = id % KCH;
-            *(uint4*)(Ks + k_off(row, ch)) = r.k[i];
-            *(uint4*)(Vs + v_off(row, ch)) = r.v[i];
-        }
-    }
-};
-
-// V stored transposed (V^T) with 256-byte rows, for 16-byte PV operand reads.
-template <int D>
-struct KvTileVt {
-    static constexpr int KCH = D / 8;                   // 16-byte chunks per K row
-    static constexpr int HALF = BN / 2;                 // keys staged by one wave group
-    static constexpr int K_LOADS = HALF * KCH / GT;     // 16-byte K loads per thread
-    static constexpr int V_UNITS = (HALF / 2) * KCH;    // (2 keys x 8 dims) V units per half tile
-    static constexpr int K_ELEMS = BN * D;
-    static constexpr int VT_STRIDE = 2 * BN;            // V^T row pitch in elements (256 bytes)
-    static constexpr int V_ELEMS = D * VT_STRIDE;
-    static_assert(K_LOADS >= 1 && K_LOADS <= 2 && HALF * KCH % GT == 0 && V_UNITS <= GT, "tile split");
-
-    // K, row-major: chunk c of row r lives at chunk c ^ (r mod KCH); the 32
-    // rows x 2 chunks of one MFMA operand read hit every bank equally.
     static __device__ __forceinline__ int k_off(int row, int ch) {
-        return row * D + ((ch ^ (row & (KCH - 1))) << 3);
+        return row * D + ((ch ^ k_swz(row)) << 3);
     }
-    // V^T: one row per head dimension, BN keys used out of a 256-byte pitch;
-    // 8-key chunk c of row d lives at chunk c ^ (d mod 16) ^ ((d >> 4) mod 8).
-    // Measured with the LDS bank-conflict counter, the PV operand read (32
-    // consecutive dims x 2 chunks) is conflict-free; the staging writes below
-    // (4 bytes = 2 keys of one dim, dims 8c+j of the 16 chunks c) cover 64
-    // distinct banks.  With the (d mod 16) term alone 8-byte transposed
-    // writes conflict 16-way.
-    static __device__ __forceinline__ int vt_off(int dim, int ch) {
-        return dim * VT_STRIDE + ((ch ^ (dim & 15) ^ ((dim >> 4) & 7)) << 3);
+    static __device__ __forceinline__ int v_off(int row, int ch) {
+        return row * D + ((ch ^ v_swz(row)) << 3);
     }
 
-    // Staging of one wave group's half tile (keys 32*grp .. 32*grp+31).  Every
-    // thread carries K_LOADS 16-byte chunks of K and one unit of V: 2
-    // consecutive keys x 8 dims, transposed in registers on the way to LDS.
-    struct Regs {
-        uint4 k0, k1, v0, v1;
+    // Tile rows [0, BN) global -> LDS with no registers in between: lane l of
+    // wave w fills 16-byte chunk NT*r + 64*w + l of the buffer, so it loads
+    // the global chunk the swizzle puts there.  Round r covers the rows of
+    // round 0 plus r*NT/KCH, a multiple of KCH, so both swizzles repeat and
+    // Offs holds only round 0's byte offsets (from the tile's first row).
+    static constexpr int ROWS_PER_ROUND = NT / KCH;
+    static_assert(ROWS_PER_ROUND % KCH == 0 && ROWS_PER_ROUND % 4 == 0, "swizzles repeat per round");
+    struct Offs {
+        uint32_t k, v;
     };
-
-    static __device__ __forceinline__ void load(Regs& r, const uint16_t* Kb, const uint16_t* Vb,
-                                                int64_t row_stride, int klen, int grp, int gt) {
-        {
-            const int row = HALF * grp + gt / KCH, ch = gt % KCH;
-            r.k0 = row < klen ? *(const uint4*)(Kb + row * row_stride + ch * 8) : make_uint4(0, 0, 0, 0);
-        }
-        if (K_LOADS > 1) {
-            const int id = gt + GT;
-            const int row = HALF * grp + id / KCH, ch = id % KCH;
-            r.k1 = row < klen ? *(const uint4*)(Kb + row * row_stride + ch * 8) : make_uint4(0, 0, 0, 0);
-        }
-        if (gt < V_UNITS) {
-            const int ch = gt % KCH, kp = gt / KCH;
-            const int row = HALF * grp + 2 * kp;
-            r.v0 = row < klen ? *(const uint4*)(Vb + row * row_stride + ch * 8) : make_uint4(0, 0, 0, 0);
-            r.v1 = row + 1 < klen ? *(const uint4*)(Vb + (row + 1) * row_stride + ch * 8)
-                                  : make_uint4(0, 0, 0, 0);
-        }
+    static __device__ __forceinline__ uint32_t chunk_off(int r, int w, int lane, int rows_in,
+                                                         uint32_t row_bytes, bool is_v) {
+        const int c = NT * r + 64 * w + lane;
+        const int row = c / KCH, slot = c % KCH;
+        const int sw = is_v ? v_swz(row) : k_swz(row);
+        return (row < rows_in ? (uint32_t)row * row_bytes : 0u) + (uint32_t)((slot ^ sw) << 4);
     }
-
-    static __device__ __forceinline__ void store(const Regs& r, uint16_t* Ks, uint16_t* Vts, int grp,
-                                                 int gt) {
-        {
-            const int row = HALF * grp + gt / KCH, ch = gt % KCH;
-            *(uint4*)(Ks + k_off(row, ch)) = r.k0;
-        }
-        if (K_LOADS > 1) {
-            const int id = gt + GT;
-            const int row = HALF * grp + id / KCH, ch = id % KCH;
-            *(uint4*)(Ks + k_off(row, ch)) = r.k1;
-        }
-        if (gt < V_UNITS) {
-            const int ch = gt % KCH, kp = gt / KCH;
-            const int key0 = HALF * grp + 2 * kp;  // keys key0, key0+1; dims 8ch..8ch+7
-            const uint32_t a[4] = {r.v0.x, r.v0.y, r.v0.z, r.v0.w};
-            const uint32_t b[4] = {r.v1.x, r.v1.y, r.v1.z, r.v1.w};
+    static __device__ __forceinline__ Offs offsets(int w, int lane, uint32_t row_bytes) {
+        Offs o;
+        o.k = chunk_off(0, w, lane, BN, row_bytes, false);
+        o.v = chunk_off(0, w, lane, BN, row_bytes, true);
+        return o;
+    }
+    // Rows at or past klen (the ragged end of a chunk) repeat row 0: finite
+    // data under keys that the mask removes.
+    static __device__ __forceinline__ void load(const uint16_t* Kb, const uint16_t* Vb, const Offs& o,
+                                                int klen, uint32_t row_bytes, const uint16_t* Ks,
+                                                const uint16_t* Vs, int w, int lane) {
+        if (klen >= BN) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                // dword j of a key row holds dims 2j (low half) and 2j+1 (high half)
-                const int d0 = 8 * ch + 2 * j;
-                *(uint32_t*)(Vts + vt_off(d0, key0 >> 3) + (key0 & 7)) =
-                    __builtin_amdgcn_perm(b[j], a[j], 0x05040100u);
-                *(uint32_t*)(Vts + vt_off(d0 + 1, key0 >> 3) + (key0 & 7)) =
-                    __builtin_amdgcn_perm(b[j], a[j], 0x07060302u);
+            for (int r = 0; r < ROUNDS; ++r) {
+                const int64_t ro = (int64_t)r * ROWS_PER_ROUND * (row_bytes / 2);
+                lds_dma16(Kb + ro, o.k, lds_addr(Ks + (NT * r + 64 * w) * 8));
+                lds_dma16(Vb + ro, o.v, lds_addr(Vs + (NT * r + 64 * w) * 8));
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < ROUNDS; ++r) {
+                lds_dma16(Kb, chunk_off(r, w, lane, klen, row_bytes, false),
+                          lds_addr(Ks + (NT * r + 64 * w) * 8));
+                lds_dma16(Vb, chunk_off(r, w, lane, klen, row_bytes, true),
+                          lds_addr(Vs + (NT * r + 64 * w) * 8));
             }
         }
     }
 };
-
-#if RA_FWD_VT
-template <int D> using KvTile = KvTileVt<D>;
-#else
-template <int D> using KvTile = KvTileRow<D>;
-#endif
 
 __device__ __forceinline__ i16x4 ds_read_tr(const uint16_t* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
@@ -217,7 +162,7 @@ __device__ __forceinline__ int swap_bits23(int m) {
     return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
 }
 
-// max / sum of a value over the two half-waves (lanes l and l^32)
+// max / sum / or of a value over the two half-waves (lanes l and l^32)
 __device__ __forceinline__ float halves_max(float x) {
     const unsigned u = __builtin_bit_cast(unsigned, x);
     const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
@@ -228,46 +173,141 @@ __device__ __forceinline__ float halves_sum(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
     return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
 }
+__device__ __forceinline__ bool halves_any(bool b) {
+    const unsigned u = b ? 1u : 0u;
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return ((unsigned)r[0] | (unsigned)r[1]) != 0u;
+}
 
-struct TileDesc {
-    int64_t krow;  // first K/V row (sharded order)
-    int64_t kpos;  // global position of that row
-    int klen;      // valid rows of the tile (ragged end of a chunk)
+// ----------------------------------------------------------------------------
+// Key-tile cursor, in ring order: step t = 0..P-1 visits shard (rank - t) mod
+// P (K/V travel r -> r+1, lesson 8 section 2), its chunks in local order and
+// each chunk's tiles in ascending order; under the causal mask only the
+// prefix of a chunk up to the tile's last query position is visited.  The
+// same order as the generic iterator of the other kernels, in 32-bit fields
+// (positions < 2^30): advancing inside a segment is three adds, the segment
+// walk runs only at its end.  All fields are uniform across the work-group.
+// ----------------------------------------------------------------------------
+struct KvCur {
+    int t, lc;   // ring step and local chunk of the current segment
+    int tl;      // tiles of the segment after the current one
+    int krow;    // first K/V row (sharded order) of the current tile
+    int kpos;    // global position of that row
+    int cleft;   // rows of the chunk from that row on
 };
 
-__device__ __forceinline__ TileDesc tile_desc(const FwdParams& p, const KvIter& it) {
-    TileDesc d;
-    const int64_t off = (int64_t)it.tile * BN;
-    d.krow = it.krow + off;
-    d.kpos = it.kpos + off;
-    const int64_t left = p.c - off;
-    d.klen = left < BN ? (int)left : BN;
-    return d;
+__device__ __forceinline__ bool cur_seg(const FwdParams& p, int rank, int qmax, KvCur& c) {
+    int s = rank - c.t;
+    if (s < 0) s += p.P;
+    const int cl = (int)p.c;
+    const int gch = c.lc ? 2 * p.P - 1 - s : s;  // lc = 1 only for the zig-zag split
+    c.krow = s * (int)p.n + c.lc * cl;
+    c.kpos = gch * cl;
+    int vis = cl;
+    if (p.causal) vis = min(max(qmax - c.kpos + 1, 0), cl);
+    c.tl = (vis + BN - 1) / BN - 1;
+    c.cleft = cl;
+    return c.tl >= 0;
+}
+
+// next non-empty segment; only called while tiles remain
+__device__ __forceinline__ void cur_skip(const FwdParams& p, int rank, int qmax, KvCur& c) {
+    do {
+        if (++c.lc == p.chunks_per_rank) {
+            c.lc = 0;
+            ++c.t;
+        }
+    } while (c.t < p.P && !cur_seg(p, rank, qmax, c));
+}
+
+__device__ __forceinline__ void cur_first(const FwdParams& p, int rank, int qmax, KvCur& c) {
+    c.t = 0;
+    c.lc = 0;
+    if (!cur_seg(p, rank, qmax, c)) cur_skip(p, rank, qmax, c);
+}
+
+__device__ __forceinline__ void cur_next(const FwdParams& p, int rank, int qmax, KvCur& c) {
+    if (c.tl > 0) {
+        --c.tl;
+        c.krow += BN;
+        c.kpos += BN;
+        c.cleft -= BN;
+    } else {
+        cur_skip(p, rank, qmax, c);
+    }
+}
+
+__device__ __forceinline__ int cur_count(const FwdParams& p, int rank, int qmax) {
+    KvCur c;
+    int n = 0;
+    for (c.t = 0; c.t < p.P; ++c.t)
+        for (c.lc = 0; c.lc < p.chunks_per_rank; ++c.lc)
+            if (cur_seg(p, rank, qmax, c)) n += c.tl + 1;
+    return n;
+}
+
+// Masks keys of a tile outside the query's causal window or past a ragged
+// chunk end.  Register r of block kb2 holds key kb2*32 + 16*(r/8) + 8h + r%8.
+__device__ __forceinline__ void mask_tile(f32x16 (&s)[2], int lim) {
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int k0 = kb2 * 32 + 16 * (r >> 3) + (r & 7);
+            s[kb2][r] = k0 < lim ? s[kb2][r] : kNegInf;
+        }
+}
+
+// P = exp2(S*c - mu), its exact and bf16-rounded sums.
+__device__ __forceinline__ void exp_tile(const f32x16 (&s)[2], float c, float mu, bf16x8 (&pb)[4],
+                                         float& lsum, float& lrsum) {
+    const bf16x2 kOnes = {(__bf16)1.0f, (__bf16)1.0f};
+    lsum = 0.f;
+    lrsum = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int i2 = 0; i2 < 8; i2 += 2) {
+            const float e0 = fast_exp2(__builtin_fmaf(s[kk >> 1][8 * (kk & 1) + i2], c, -mu));
+            const float e1 = fast_exp2(__builtin_fmaf(s[kk >> 1][8 * (kk & 1) + i2 + 1], c, -mu));
+            lsum += e0 + e1;
+            bf16x2 pr;
+            pr[0] = (__bf16)e0;
+            pr[1] = (__bf16)e1;
+            lrsum = __builtin_amdgcn_fdot2_f32_bf16(pr, kOnes, lrsum, false);
+            pb[kk][i2] = pr[0];
+            pb[kk][i2 + 1] = pr[1];
+        }
 }
 
 template <int D>
 __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdParams p) {
     using T = KvTile<D>;
-    constexpr int KB = D / 16;  // MFMA k-blocks of Q K^T
-    constexpr int DB = D / 32;  // 32-dim blocks of O^T
-    __shared__ __attribute__((aligned(16))) uint16_t ldsK[NBUF][T::K_ELEMS];
-    __shared__ __attribute__((aligned(16))) uint16_t ldsV[NBUF][T::V_ELEMS];  // V^T, padded rows
+    constexpr int KB = D / 16;    // MFMA k-blocks of Q K^T
+    constexpr int DB = D / 32;    // 32-dim blocks of O^T
+    constexpr int NQK = 2 * KB;   // K operands (MFMAs) of S^T per tile
+    constexpr int NPV = 4 * DB;   // V operands (MFMAs) of O^T per tile
+    constexpr int NMF = NQK + NPV;
+    constexpr int AHEAD = RA_FWD_AHEAD;
+    static_assert(AHEAD >= 1 && AHEAD <= NQK, "read-ahead depth");
+    // 1 KB alignment leaves the low ten address bits to the in-tile offset,
+    // so the swizzle XORs below can act on absolute LDS addresses
+    __shared__ __attribute__((aligned(1024))) uint16_t ldsK[NBUF][T::ELEMS];
+    __shared__ __attribute__((aligned(1024))) uint16_t ldsV[NBUF][T::ELEMS];
 
     const QTile qt = decode_qtile<BM>(p, blockIdx.x);
     const int t = threadIdx.x;
     const int lane = t & 63;
     const int w = __builtin_amdgcn_readfirstlane(t >> 6);  // wave index, uniform in the wave
     const int h = lane >> 5, m = lane & 31;
-    const int grp = w >> 2, gt = t & (GT - 1);  // wave group; one wave of each per SIMD
 
     // this lane's query (MFMA column m of the wave's 32 queries)
     const int qi = w * 32 + m;
-    const bool qvalid = qi < qt.rows;
-    const int64_t qpos = qt.pos0 + qi;
-    const int wrows = qt.rows - w * 32;  // valid queries of this wave (may be <= 0)
-    const int64_t wq_lo = qt.pos0 + w * 32;
-    const int64_t wq_hi = wq_lo + (wrows < 32 ? wrows : 32) - 1;
-    const int64_t qmax = qt.pos0 + qt.rows - 1;
+    const int pos0 = (int)qt.pos0;
+    const int qpos = pos0 + qi;
+    const int wq_lo = pos0 + w * 32;
+    const int qmax = pos0 + qt.rows - 1;
+    const float c = p.scale_log2;
 
     bf16x8 qop[KB];
     {
@@ -275,7 +315,7 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdParams p) {
                              ((qt.b * p.q_rows + qt.q_row0 + qi) * p.Hq + qt.qh) * (int64_t)D;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
-            uint4 u = qvalid ? *(const uint4*)(qp + kb * 16 + h * 8) : make_uint4(0, 0, 0, 0);
+            const uint4 u = qi < qt.rows ? *(const uint4*)(qp + kb * 16 + h * 8) : make_uint4(0, 0, 0, 0);
             qop[kb] = __builtin_bit_cast(bf16x8, u);
         }
     }
@@ -285,209 +325,225 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdParams p) {
     for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
-    float m_run = kNegInf, l_run = 0.f, lr_run = 0.f;
-    const bf16x2 kOnes = {(__bf16)1.0f, (__bf16)1.0f};
+    float m_ref = kNegInf, l_run = 0.f, lr_run = 0.f;
+    f32x16 zero16;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) zero16[r] = 0.f;
 
     const int64_t row_stride = (int64_t)p.Hkv * D;
+    const uint32_t row_bytes = (uint32_t)(row_stride * 2);
     const uint16_t* Kg = (const uint16_t*)p.K + ((int64_t)qt.b * p.S * p.Hkv + qt.kvh) * D;
     const uint16_t* Vg = (const uint16_t*)p.V + ((int64_t)qt.b * p.S * p.Hkv + qt.kvh) * D;
+    const typename T::Offs offs = T::offsets(w, lane, row_bytes);
 
-    // ---- prologue: tile 0 in LDS (both halves), group 1's half of tile 1 in
-    // LDS, and each group's next half-tile (1 + grp) in registers
-    const int n = kv_count(p, qt.rank, qmax, BN);
-    KvIter it_c, it_l;
-    typename T::Regs regs;
+    // ---- prologue: tiles 0 and 1 on their way into buffers 0 and 1; the V
+    // buffer "before" tile 0 zeroed (the first PV product multiplies P = 0)
+    const int n = cur_count(p, qt.rank, qmax);
+    KvCur it_c, it_l;  // tile i of the loop; last tile whose loads were issued
+    int issued = 0;    // tiles whose loads were issued
     if (n > 0) {
-        kv_first(p, qt.rank, qmax, BN, it_c);
+        cur_first(p, qt.rank, qmax, it_c);
         it_l = it_c;
-        TileDesc d0 = tile_desc(p, it_c);
-        T::load(regs, Kg + d0.krow * row_stride, Vg + d0.krow * row_stride, row_stride, d0.klen, grp, gt);
-        T::store(regs, ldsK[0], ldsV[0], grp, gt);
-        for (int j = 1; j <= 1 + grp && j < n; ++j) {
-            kv_next(p, qt.rank, qmax, BN, it_l);
-            const TileDesc dj = tile_desc(p, it_l);
-            T::load(regs, Kg + dj.krow * row_stride, Vg + dj.krow * row_stride, row_stride, dj.klen,
-                    grp, gt);
-            if (j < 1 + grp) T::store(regs, ldsK[j], ldsV[j], grp, gt);
+        T::load(Kg + it_l.krow * row_stride, Vg + it_l.krow * row_stride, offs, min(it_l.cleft, BN),
+                row_bytes, ldsK[0], ldsV[0], w, lane);
+        issued = 1;
+        for (int j = 1; j < 2 && j < n; ++j) {
+            cur_next(p, qt.rank, qmax, it_l);
+            T::load(Kg + it_l.krow * row_stride, Vg + it_l.krow * row_stride, offs, min(it_l.cleft, BN),
+                    row_bytes, ldsK[j], ldsV[j], w, lane);
+            issued = j + 1;
         }
     }
-    // the first MFMA phase multiplies P = 0 by the V buffer "before" tile 0:
-    // zero it so no stale bits (NaN patterns) reach the accumulators
-    for (int e = t * 8; e < T::V_ELEMS; e += NT * 8)
+    for (int e = t * 8; e < T::ELEMS; e += NT * 8)
         *(uint4*)(&ldsV[NBUF - 1][e]) = make_uint4(0, 0, 0, 0);
-    // Drain the prologue's loads here: otherwise the wait-count analysis merges
-    // them into the loop header and makes the loop wait on in-flight staging
-    // loads at its first MFMA.
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    __syncthreads();
-    if (grp == 1) __syncthreads();  // group 1 runs one phase behind group 0
 
-    // P of the previous tile (zero before the first tile, whose "previous" V
-    // buffer is zeroed in the prologue, so the first PV product adds 0)
-    bf16x8 pb[4];
+    // LDS operand addresses.  Both chunk swizzles are XORs into address bits
+    // that the row part leaves clear, so the byte address of an operand is
+    // (per-lane base) ^ (constant of its dim block) + (constant of its row
+    // block and buffer): one base register per tensor and one v_xor per read.
+    //
+    // K operand j: keys 32*(j%2).. (rows permuted), dims 16*(j/2)..: the two
+    // S^T accumulators alternate, so consecutive MFMAs are independent.  Lane
+    // (h, m) reads row 32*(j%2) + swap(m), 16-byte chunk 2*(j/2) + h, stored
+    // at chunk (2*(j/2) + h) ^ (row mod KCH) = 2*(j/2) ^ (h ^ (swap(m) mod KCH)).
+    typedef __attribute__((address_space(3))) const char lds_char;
+    const int sm = swap_bits23(m);
+    uint32_t kbase = lds_addr(ldsK) + (uint32_t)(sm * 2 * D + 16 * (h ^ (sm & (T::KCH - 1))));
+    // V operand j: keys 16*(j/DB).., dims 32*(j%DB)..; lane l of 16-lane group
+    // g points at row 8*(g>>1) + (l%16)/4 (+4 for the second read) and dims
+    // 16*(g&1) + 4*(l%4); it receives 4 consecutive keys of one dim.  The
+    // swizzle flips the 64-byte dim block by v_swz(row)/4, which depends only
+    // on the row bits that this base fixes.
+    const int vr = 8 * h + ((lane & 15) >> 2);
+    uint32_t vbase = lds_addr(ldsV) + (uint32_t)(vr * 2 * D + 64 * (T::v_swz(vr) >> 2) +
+                                                 16 * (2 * ((lane >> 4) & 1) + ((lane & 3) >> 1)) +
+                                                 8 * (lane & 1));
+    // operand j of ring buffer b (b known at compile time)
+    auto read_k = [&](int j, int b) -> bf16x8 {
+        const uint32_t a = (kbase ^ (uint32_t)(32 * (j >> 1))) + (uint32_t)(b * T::ELEMS * 2 + (j & 1) * 64 * D);
+        return *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)a;
+    };
+    auto read_v = [&](int j, int b) -> bf16x8 {
+        const uint32_t a = (vbase ^ (uint32_t)(64 * (j % DB))) + (uint32_t)(b * T::ELEMS * 2 + (j / DB) * 32 * D);
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(uintptr_t)a);
+        const i16x4 hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(uintptr_t)(a + 8 * D));
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+
+    // tile 0 resident (tile 1 may be in flight); its scores
+    f32x16 sa[2], sb[2];  // S of tiles i and i+1 (roles swap every iteration)
+    bf16x8 pa[4], pb[4];  // P of tiles i-1 and i (roles swap every iteration)
+    if (issued > 1)
+        __builtin_amdgcn_s_waitcnt(0x0F70 | T::LOADS);
+    else
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    if (n > 0) {
+#pragma unroll
+        for (int j = 0; j < NQK; ++j) {
+            const bf16x8 a = read_k(j, 0);
+            sa[j & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[j >> 1], j < 2 ? zero16 : sa[j & 1], 0, 0, 0);
+        }
+    }
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-        for (int i2 = 0; i2 < 8; ++i2) pb[kk][i2] = (__bf16)0.f;
+        for (int i2 = 0; i2 < 8; ++i2) pa[kk][i2] = (__bf16)0.f;
 
-    // MFMA phase operands, in issue order: NPV blocks of O^T += V^T P^T (block
-    // j: keys 16*(j/DB).., dims 32*(j%DB)..), then NQK blocks of S^T = K Q^T
-    // (block j: keys 32*(j/KB).., dims 16*(j%KB)..).  Each operand is one
-    // 16-byte LDS read.
-    constexpr int NPV = 4 * DB, NQK = 2 * KB, NMF = NPV + NQK;
-    auto read_op = [&](int j, int buf) -> bf16x8 {
-        if (j < NPV) {
-            const int kk = j / DB, db = j % DB;
-#if RA_FWD_VT
-            return *(const bf16x8*)(ldsV[(buf + NBUF - 1) % NBUF] + T::vt_off(db * 32 + m, 2 * kk + h));
-#else
-            // transpose reads: lane l of 16-lane group g points at row
-            // 8*(g>>1) + (l%16)/4 (+4 for the second read) and dims
-            // 16*(g&1) + 4*(l%4); it receives 4 consecutive keys of one dim
-            const uint16_t* Vs = ldsV[(buf + NBUF - 1) % NBUF];
-            const int r0 = 16 * kk + 8 * (lane >> 5) + ((lane & 15) >> 2);
-            const int col = db * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-            const i16x4 lo = ds_read_tr(Vs + T::v_off(r0, col >> 3) + (col & 7));
-            const i16x4 hi = ds_read_tr(Vs + T::v_off(r0 + 4, col >> 3) + (col & 7));
-            return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-#endif
-        }
-        const int q = j - NPV, kb2 = q / KB, kb = q % KB;
-        const int row = kb2 * 32 + swap_bits23(m);
-        return *(const bf16x8*)(ldsK[buf] + T::k_off(row, kb * 2 + h));
-    };
-
-    constexpr int AHEAD = RA_FWD_AHEAD;  // operands read ahead of their MFMA
-    for (int i = 0; i < n; ++i) {
-        // ================= MFMA phase: O += V_{i-1} P_{i-1}; S_i = K_i Q^T
-        // One straight-line block: every wave runs both products on every
-        // tile (a tile wholly in the future of a wave's queries is masked to
-        // P = 0 in the VALU phase), so the operand reads can be issued AHEAD
-        // MFMAs early and their LDS latency hides behind the matrix pipe.
-        const TileDesc dc = tile_desc(p, it_c);
-        const int cb = i % NBUF;
-        f32x16 sacc[2];
-#pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) sacc[kb2][r] = 0.f;
-        bf16x8 ops[AHEAD];
-#pragma unroll
-        for (int j = 0; j < AHEAD; ++j) ops[j] = read_op(j, cb);
-#if RA_FWD_PIN
-        // pin the issue order: the first AHEAD operands' reads, then per MFMA
-        // the read of the operand AHEAD positions later
-        __builtin_amdgcn_sched_group_barrier(0x100, RA_FWD_VT ? AHEAD : 2 * AHEAD, 0);
-#endif
-#pragma unroll
-        for (int j = 0; j < NMF; ++j) {
-            const bf16x8 a = ops[j % AHEAD];
-            if (j + AHEAD < NMF) ops[j % AHEAD] = read_op(j + AHEAD, cb);
-            if (j < NPV) {
-                oacc[j % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[j / DB], oacc[j % DB], 0, 0, 0);
-            } else {
-                const int q = j - NPV;
-                sacc[q / KB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[q % KB], sacc[q / KB], 0, 0, 0);
-            }
-#if RA_FWD_PIN
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            if (!RA_FWD_VT && j + AHEAD < NPV)
-                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-            else if (j + AHEAD < NMF)
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-#endif
-        }
+    // One iteration: tile i, with i % NBUF == SLOT known at compile time.
+    // sc / sn: S of tiles i / i+1; pp / pc: P of tiles i-1 / i.
+    auto iteration = [&](auto slot, int i, f32x16 (&sc)[2], f32x16 (&sn)[2], bf16x8 (&pp)[4],
+                         bf16x8 (&pc)[4]) {
+        constexpr int SLOT = decltype(slot)::value;
+        // tile i+1 resident; the buffer of tile i-2 is free for tile i+2
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         __syncthreads();
+        if (issued < n) {
+            cur_next(p, qt.rank, qmax, it_l);
+            T::load(Kg + it_l.krow * row_stride, Vg + it_l.krow * row_stride, offs, min(it_l.cleft, BN),
+                    row_bytes, ldsK[(SLOT + 2) % NBUF], ldsV[(SLOT + 2) % NBUF], w, lane);
+            ++issued;
+        }
+        // S_{i+1} from buffer (i+1) (stale data past the last tile: unused)
+        constexpr int KBUF = (SLOT + 1) % NBUF, VBUF = (SLOT + NBUF - 1) % NBUF;
 
-        // ================= VALU phase: softmax of S_i; stage K/V rows
+        const int klen = min(it_c.cleft, BN);
+        if (klen < BN || (p.causal && it_c.kpos + BN - 1 > wq_lo)) {
+            const int lim = p.causal ? min(max(qpos - it_c.kpos + 1, 0), klen) : klen;
+            mask_tile(sc, lim - 8 * h);
+        }
+        // The stage, slot by slot: MFMA slot j is QK operand j/2 (even j) or
+        // PV operand j/2 (odd j); behind it the softmax runs one element per
+        // slot as a three-step pipeline (FMA of element j+1, exp of element
+        // j, sums and bf16 packing of element j-1), so exactly one exp and
+        // about three other VALU instructions trail each MFMA and only a few
+        // temporaries are live.  sched_barrier keeps this order.
+        float lsum = 0.f, lrsum = 0.f;
         {
-            // mask (diagonal / ragged tiles only): register r of block kb2
-            // holds key kb2*32 + 16*(r/8) + 8h + (r%8); keys >= lim are masked
-            const bool need_mask = dc.klen < BN || (p.causal && dc.kpos + BN - 1 > wq_lo);
-            if (need_mask) {
-                int lim = dc.klen;
-                if (p.causal) {
-                    const int64_t vis = qpos - dc.kpos + 1;
-                    lim = vis < (int64_t)lim ? (vis < 0 ? 0 : (int)vis) : lim;
+            // recompute the operand addresses in every stage rather than hold
+            // twelve of them in registers
+            asm volatile("" : "+v"(kbase), "+v"(vbase));
+            const float mu = m_ref == kNegInf ? 0.f : m_ref;
+            const bf16x2 kOnes = {(__bf16)1.0f, (__bf16)1.0f};
+            constexpr int NE = 32;            // softmax elements per lane and tile
+            constexpr int EPS = NE / NMF;     // elements per MFMA slot
+            static_assert(NQK == NPV && EPS * NMF == NE, "slot layout");
+            auto read_op = [&](int j) -> bf16x8 { return (j & 1) ? read_v(j >> 1, VBUF) : read_k(j >> 1, KBUF); };
+            auto sval = [&](int e) -> float { return sc[e >> 4][e & 15]; };
+            float tf[NE], ex[NE];
+            bf16x8 ops[AHEAD];
+#pragma unroll
+            for (int j = 0; j < AHEAD; ++j) ops[j] = read_op(j);
+#pragma unroll
+            for (int q = 0; q < EPS; ++q) tf[q] = __builtin_fmaf(sval(q), c, -mu);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j <= NMF; ++j) {
+                if (j < NMF) {
+                    const bf16x8 a = ops[j % AHEAD];
+                    const int q = j >> 1;
+                    if ((j & 1) == 0)
+                        sn[q & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[q >> 1], q < 2 ? zero16 : sn[q & 1],
+                                                                            0, 0, 0);
+                    else
+                        oacc[q % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pp[q / DB], oacc[q % DB], 0, 0, 0);
+                    if (j + AHEAD < NMF) ops[j % AHEAD] = read_op(j + AHEAD);
                 }
-                lim -= 8 * h;
 #pragma unroll
-                for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int k0 = kb2 * 32 + 16 * (r >> 3) + (r & 7);
-                        sacc[kb2][r] = k0 < lim ? sacc[kb2][r] : kNegInf;
+                for (int q = 0; q < EPS; ++q) {
+                    const int e1 = (j + 1) * EPS + q, e0 = j * EPS + q, em = (j - 1) * EPS + q;
+                    if (e1 < NE) tf[e1] = __builtin_fmaf(sval(e1), c, -mu);
+                    if (e0 < NE) ex[e0] = fast_exp2(tf[e0]);
+                    if (em >= 0 && em < NE) {
+                        lsum += ex[em];
+                        if (em & 1) {
+                            bf16x2 pr;
+                            pr[0] = (__bf16)ex[em - 1];
+                            pr[1] = (__bf16)ex[em];
+                            lrsum = __builtin_amdgcn_fdot2_f32_bf16(pr, kOnes, lrsum, false);
+                            pc[em >> 3][(em & 7) - 1] = pr[0];
+                            pc[em >> 3][em & 7] = pr[1];
+                        }
                     }
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
+        }
+        // rare: a lane's sum exceeded the cap, or its first finite score
+        const bool slow = lsum > kSumCap || (m_ref == kNegInf && lsum > 0.f);
+        if (__builtin_amdgcn_ballot_w64(slow) != 0) {
+            const bool need = halves_any(slow);
             float mx = kNegInf;
 #pragma unroll
             for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb2][r]);
-            mx = halves_max(mx) * p.scale_log2;
-            const bool move = mx > m_run + kLazy;
-            const float m_ref = move ? mx : m_run;
-            const float m_use = m_ref == kNegInf ? 0.f : m_ref;
-            if (__builtin_amdgcn_ballot_w64(move) != 0) {
-                const float alpha = fast_exp2(m_run - m_use);
-                l_run *= alpha;
-                lr_run *= alpha;
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb2][r]);
+            mx = halves_max(mx) * c;
+            const float m_new = need ? fmaxf(m_ref, mx) : m_ref;
+            const float alpha = need ? fast_exp2(m_ref - m_new) : 1.f;  // 0 when m was -inf
+            l_run *= alpha;
+            lr_run *= alpha;
 #pragma unroll
-                for (int db = 0; db < DB; ++db)
+            for (int db = 0; db < DB; ++db)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-            }
-            m_run = m_ref;
-            // l_run sums the exponentials exactly (for the LSE); lr_run sums
-            // the bf16-rounded values the PV product uses (for O), so a
-            // dominant key's rounding cancels in O = sum(p V) / sum(p)
-            float lsum = 0.f;
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-                for (int i2 = 0; i2 < 8; i2 += 2) {
-                    const float e0 = fast_exp2(
-                        __builtin_fmaf(sacc[kk >> 1][8 * (kk & 1) + i2], p.scale_log2, -m_use));
-                    const float e1 = fast_exp2(
-                        __builtin_fmaf(sacc[kk >> 1][8 * (kk & 1) + i2 + 1], p.scale_log2, -m_use));
-                    lsum += e0 + e1;
-                    bf16x2 pr;
-                    pr[0] = (__bf16)e0;
-                    pr[1] = (__bf16)e1;
-                    lr_run = __builtin_amdgcn_fdot2_f32_bf16(pr, kOnes, lr_run, false);
-                    pb[kk][i2] = pr[0];
-                    pb[kk][i2 + 1] = pr[1];
-                }
-            l_run += lsum;
+                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+            m_ref = m_new;
+            exp_tile(sc, c, m_new == kNegInf ? 0.f : m_new, pc, lsum, lrsum);
         }
-        // this group's half of tile i+1+grp -> LDS; then the next half-tile's loads
-        const int wi = i + 1 + grp;
-        if (wi < n) {
-            T::store(regs, ldsK[wi % NBUF], ldsV[wi % NBUF], grp, gt);
-            if (wi + 1 < n) {
-                kv_next(p, qt.rank, qmax, BN, it_l);
-                const TileDesc dl = tile_desc(p, it_l);
-                T::load(regs, Kg + dl.krow * row_stride, Vg + dl.krow * row_stride, row_stride,
-                        dl.klen, grp, gt);
-            }
-        }
-        __syncthreads();
-        if (i + 1 < n) kv_next(p, qt.rank, qmax, BN, it_c);
+        l_run += lsum;
+        lr_run += lrsum;
+        if (i + 1 < n) cur_next(p, qt.rank, qmax, it_c);
+    };
+
+    static_assert(NBUF == 4, "the loop body is unrolled over the ring");
+    for (int i = 0; i < n; i += 4) {
+        iteration(std::integral_constant<int, 0>(), i, sa, sb, pa, pb);
+        if (i + 1 < n) iteration(std::integral_constant<int, 1>(), i + 1, sb, sa, pb, pa);
+        if (i + 2 < n) iteration(std::integral_constant<int, 2>(), i + 2, sa, sb, pa, pb);
+        if (i + 3 < n) iteration(std::integral_constant<int, 3>(), i + 3, sb, sa, pb, pa);
     }
-    // last MFMA phase: O += V_{n-1} P_{n-1}
+    if (n > 0 && (n - 1) % 2 == 0) {
+        // the last tile's P is in the second copy: move it to the first
 #pragma unroll
-    for (int j = 0; j < NPV; ++j) {
-        const bf16x8 a = read_op(j, n % NBUF);
-        oacc[j % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[j / DB], oacc[j % DB], 0, 0, 0);
+        for (int kk = 0; kk < 4; ++kk) pa[kk] = pb[kk];
     }
-    __syncthreads();
-    if (grp == 0) __syncthreads();  // matches group 1's extra barrier
+
+    // ---- epilogue: O += V_{n-1} P_{n-1}
+    if (n > 0) {
+        const int vb = (n - 1) % NBUF;
+#pragma unroll
+        for (int j = 0; j < NPV; ++j) {
+            const bf16x8 a = read_v(j, vb);
+            oacc[j % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pa[j / DB], oacc[j % DB], 0, 0, 0);
+        }
+    }
 
     // ---- finalize: O = O / l, LSE = m + ln l (natural log)
     const float l_tot = halves_sum(l_run);
     const float lr_tot = halves_sum(lr_run);
     const float inv = lr_tot > 0.f ? 1.f / lr_tot : 0.f;
-    if (qvalid) {
+    if (qi < qt.rows) {
         const int64_t obase = ((qt.b * p.q_rows + qt.q_row0 + qi) * p.Hq + qt.qh) * (int64_t)D;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
@@ -508,7 +564,7 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdParams p) {
                 }
             }
         if (h == 0) {
-            const float lse = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : kNegInf;
+            const float lse = l_tot > 0.f ? (m_ref + __log2f(l_tot)) * kLn2 : kNegInf;
             p.LSE[((int64_t)qt.b * p.Hq + qt.qh) * p.q_rows + qt.q_row0 + qi] = lse;
         }
     }
