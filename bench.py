@@ -36,8 +36,8 @@ METRIC = "ring-attn fwd TFLOP/s (% bf16 MFMA peak); KV-shard decode GB/s (% HBM 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-PREFILL_SOURCES = ["fwd_bf16.hip", "attn_tile.h", "ra_device.h", "ra_internal.h"]
-DECODE_SOURCES = ["decode.hip", "attn_tile.h", "ra_device.h", "ra_internal.h"]
+PREFILL_SOURCES = ["fwd_bf16.hip", "ra_device.h", "ra_internal.h"]
+DECODE_SOURCES = ["decode.hip", "ra_device.h", "ra_internal.h"]
 
 
 def log(msg: str) -> None:

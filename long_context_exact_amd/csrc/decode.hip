@@ -7,31 +7,83 @@
 // bf16 kernel: one work-group per (batch, kv head, part).  The Sq x G query
 // rows that read this kv head form the 32 MFMA columns (unused columns carry
 // zero queries and are never stored).  The part's keys stream through LDS in
-// stages of 128 (two 64-key tiles, double-buffered); each of the 4 waves
-// takes 32 keys of a stage and keeps its own (m, l, O) state; the four states
-// are merged through LDS at the end.  The kernel is bound by HBM: every K/V
-// byte is read exactly once.
-#include "attn_tile.h"
+// stages of 128; each of the 4 waves takes 32 keys of a stage and keeps its
+// own (m, l, O) state, and the four states are merged at the end.  The kernel
+// is bound by HBM (every K/V byte is read once), so what matters is the bytes
+// in flight: the next stage is loaded into registers while the current one is
+// used from a single 64 KB LDS stage, which lets two work-groups share a CU.
+// K and V stay row-major in LDS; the PV operand (8 consecutive keys of one
+// head dim) comes from two ds_read_b64_tr_b16 transposing reads.
+#include "ra_device.h"
 
 namespace ra {
 namespace {
 
 constexpr int NT = 256;
-constexpr int BN = 64;       // keys per tile
-constexpr int STAGE = 128;   // keys per stage (two tiles)
+constexpr int STAGE = 128;   // keys per stage (4 waves x 32)
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 template <int D>
-__global__ __launch_bounds__(NT) void decode_bf16_kernel(DecodeParams p) {
-    using T = Tile<D, BN, NT>;
+struct DecStage {
+    static constexpr int KCH = D / 8;                 // 16-byte chunks per row
+    static constexpr int ELEMS = STAGE * D;
+    static constexpr int LOADS = STAGE * KCH / NT;    // 16-byte loads per thread per tensor
+    static_assert(STAGE * KCH % NT == 0, "stage split");
+    // K: chunk c of row r lives at chunk c ^ (r mod KCH) (MFMA operand reads
+    // of 32 rows x 2 chunks hit every bank equally).  V: a transposing read
+    // touches 8 rows (two groups of 4) x 32 dims; the row swizzle spreads them.
+    static __device__ __forceinline__ int k_off(int row, int ch) {
+        return row * D + ((ch ^ (row & (KCH - 1))) << 3);
+    }
+    static __device__ __forceinline__ int v_off(int row, int ch) {
+        const int sw = D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
+        return row * D + ((ch ^ sw) << 3);
+    }
+    struct Regs {
+        uint4 k[LOADS], v[LOADS];
+    };
+    // rows [0, klen) of the stage from global memory; rows past klen load as
+    // 0.  Load i of thread t covers row t/KCH + i*NT/KCH, chunk t%KCH: one
+    // per-thread byte offset against a uniform base that steps NT/KCH rows.
+    static __device__ __forceinline__ void load(Regs& r, const uint16_t* Kb, const uint16_t* Vb,
+                                                int64_t row_stride, int klen, int t) {
+        const int row0 = t / KCH;
+        const uint32_t off = (uint32_t)(row0 * row_stride * 2 + (t % KCH) * 16);
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            const bool ok = row0 + i * (NT / KCH) < klen;
+            const int64_t step = (int64_t)i * (NT / KCH) * row_stride;
+            r.k[i] = ok ? *(const uint4*)((const char*)(Kb + step) + off) : make_uint4(0, 0, 0, 0);
+            r.v[i] = ok ? *(const uint4*)((const char*)(Vb + step) + off) : make_uint4(0, 0, 0, 0);
+        }
+    }
+    static __device__ __forceinline__ void store(const Regs& r, uint16_t* Ks, uint16_t* Vs, int t) {
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            const int id = t + NT * i;
+            const int row = id / KCH, ch = id % KCH;
+            *(uint4*)(Ks + k_off(row, ch)) = r.k[i];
+            *(uint4*)(Vs + v_off(row, ch)) = r.v[i];
+        }
+    }
+};
+
+template <int D>
+__global__ __launch_bounds__(NT, 2) void decode_bf16_kernel(DecodeParams p) {
+    using T = DecStage<D>;
     constexpr int KB = D / 16, DB = D / 32;
-    // [buffer][tile][K | V^T]; reused as fp32 scratch for the final merge
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][2 * T::ELEMS];
-    static_assert(sizeof(lds) >= sizeof(float) * (4 * D * 32 + 8 * 32), "merge scratch");
+    // [K | V] of one stage; reused as the scratch of the final merge
+    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * T::ELEMS];
+    static_assert(sizeof(lds) >= sizeof(float) * (3 * DB * 16 * 64 + 3 * 2 * 64), "merge scratch");
+    uint16_t* Ks = lds;
+    uint16_t* Vs = lds + T::ELEMS;
 
     const int part = blockIdx.x % p.n_parts;
     const int pair = blockIdx.x / p.n_parts;
     const int b = pair / p.Hkv, kvh = pair % p.Hkv;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int t = threadIdx.x, lane = t & 63;
+    const int w = __builtin_amdgcn_readfirstlane(t >> 6);
     const int h = lane >> 5, m = lane & 31;
     const int R = (int)p.Sq * p.G;
 
@@ -66,52 +118,39 @@ __global__ __launch_bounds__(NT) void decode_bf16_kernel(DecodeParams p) {
         for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
     float m_run = kNegInf, l_run = 0.f;
 
-    typename T::Regs regs[2];
-    auto tile_len = [&](int64_t st, int a) -> int {
-        const int64_t left = k1 - (k0 + st * STAGE + a * BN);
-        return left <= 0 ? 0 : (left < BN ? (int)left : BN);
+    auto stage_len = [&](int64_t st) -> int {
+        const int64_t left = k1 - (k0 + st * STAGE);
+        return left <= 0 ? 0 : (left < STAGE ? (int)left : STAGE);
     };
-    auto load_stage = [&](int64_t st) {
-#pragma unroll
-        for (int a = 0; a < 2; ++a) {
-            const int64_t r0 = k0 + st * STAGE + a * BN;
-            T::load(regs[a], Kg + r0 * row_stride, Vg + r0 * row_stride, row_stride, tile_len(st, a),
-                    threadIdx.x);
-        }
-    };
-    auto store_stage = [&](int buf) {
-#pragma unroll
-        for (int a = 0; a < 2; ++a) T::store(regs[a], lds[buf][a], lds[buf][a] + T::ELEMS, threadIdx.x);
-    };
-
+    typename T::Regs regs;
     if (nstages > 0) {
-        load_stage(0);
-        store_stage(0);
+        T::load(regs, Kg + k0 * row_stride, Vg + k0 * row_stride, row_stride, stage_len(0), t);
+        T::store(regs, Ks, Vs, t);
     }
     __syncthreads();
 
-    const int a = w >> 1, kb2 = w & 1;  // this wave's tile and 32-key half
-    int buf = 0;
+    const int krow = 32 * w + swap_bits23(m);   // this lane's K row (MFMA A-operand row m)
     for (int64_t st = 0; st < nstages; ++st) {
         const bool nxt = st + 1 < nstages;
-        if (nxt) load_stage(st + 1);
-        const int klen = tile_len(st, a);
-        if (klen > kb2 * 32) {
-            const uint16_t* Ks = lds[buf][a];
-            const uint16_t* Vts = lds[buf][a] + T::ELEMS;
+        if (nxt) {
+            const int64_t r0 = k0 + (st + 1) * STAGE;
+            T::load(regs, Kg + r0 * row_stride, Vg + r0 * row_stride, row_stride, stage_len(st + 1), t);
+        }
+        const int klen = stage_len(st) - 32 * w;  // this wave's valid keys (may be <= 0)
+        if (klen > 0) {
             f32x16 sacc;
 #pragma unroll
             for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
-            const int row = kb2 * 32 + swap_bits23(m);
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
-                const bf16x8 av = *(const bf16x8*)(Ks + T::k_off(row, kb * 2 + h));
+                const bf16x8 av = *(const bf16x8*)(Ks + T::k_off(krow, kb * 2 + h));
                 sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qop[kb], sacc, 0, 0, 0);
             }
-            if (klen < BN) {
+            // register r holds key 16*(r/8) + 8h + r%8 of the wave's 32
+            if (klen < 32) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int kidx = kb2 * 32 + 16 * (r >> 3) + 8 * h + (r & 7);
+                    const int kidx = 16 * (r >> 3) + 8 * h + (r & 7);
                     if (kidx >= klen) sacc[r] = kNegInf;
                 }
             }
@@ -123,11 +162,12 @@ __global__ __launch_bounds__(NT) void decode_bf16_kernel(DecodeParams p) {
             const float m_use = m_new == kNegInf ? 0.f : m_new;
             const float alpha = fast_exp2(m_run - m_use);
             float lsum = 0.f;
+            bf16x8 pb[2];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const float e = fast_exp2(__builtin_fmaf(sacc[r], p.scale_log2, -m_use));
-                sacc[r] = e;
                 lsum += e;
+                pb[r >> 3][r & 7] = (__bf16)e;
             }
             l_run = l_run * alpha + lsum;
             m_run = m_new;
@@ -135,80 +175,85 @@ __global__ __launch_bounds__(NT) void decode_bf16_kernel(DecodeParams p) {
             for (int db = 0; db < DB; ++db)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-            bf16x8 pb[2];
+            // O^T += V^T P^T: operand (kk, db) = keys 32w + 16kk.., dims 32db..;
+            // lane l of 16-lane group g reads rows 8*(g>>1) + (l%16)/4 (+4)
+            // and dims 16*(g&1) + 4*(l%4): 4 consecutive keys of one dim each
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-                for (int i = 0; i < 8; ++i) pb[kk][i] = (__bf16)sacc[8 * kk + i];
-#pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                const int dim = db * 32 + m;
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
-                    const bf16x8 av = *(const bf16x8*)(Vts + T::vt_off(dim, 2 * (2 * kb2 + kk) + h));
+                for (int db = 0; db < DB; ++db) {
+                    const int r0 = 32 * w + 16 * kk + 8 * h + ((lane & 15) >> 2);
+                    const int col = db * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+                    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) i16x4*)(Vs + T::v_off(r0, col >> 3) + (col & 7)));
+                    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) i16x4*)(Vs + T::v_off(r0 + 4, col >> 3) + (col & 7)));
+                    const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
                     oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[kk], oacc[db], 0, 0, 0);
                 }
-            }
         }
-        if (nxt) store_stage(buf ^ 1);
         __syncthreads();
-        buf ^= 1;
+        if (nxt) T::store(regs, Ks, Vs, t);
+        __syncthreads();
     }
 
-    // ---- merge the four waves' states, then write this part's (O, lse)
-    const float l_tot = xor32_sum(l_run);
-    float* scratch = (float*)&lds[0][0][0];
-    float* Ow = scratch;                 // [4][D][32]
-    float* mw = scratch + 4 * D * 32;    // [4][32]
-    float* lw = mw + 4 * 32;             // [4][32]
+    // ---- merge the four waves' states in wave 0 (same register layout in
+    // every wave, so lane l combines the other waves' lane-l values), then
+    // write this part's (O, lse)
+    float* scratch = (float*)lds;
+    float* Ow = scratch;                       // [3][DB*16][64]
+    float* ml = scratch + 3 * DB * 16 * 64;    // [3][2][64]
+    if (w > 0) {
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int dim = db * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-            Ow[(w * D + dim) * 32 + m] = oacc[db][r];
-        }
-    if (h == 0) {
-        mw[w * 32 + m] = m_run;
-        lw[w * 32 + m] = l_tot;
+            for (int r = 0; r < 16; ++r) Ow[((w - 1) * DB * 16 + db * 16 + r) * 64 + lane] = oacc[db][r];
+        ml[((w - 1) * 2 + 0) * 64 + lane] = m_run;
+        ml[((w - 1) * 2 + 1) * 64 + lane] = l_run;
     }
     __syncthreads();
-    {
-        const int n = threadIdx.x & 31;       // column
-        const int dg = threadIdx.x >> 5;      // group of D/8 dims
-        constexpr int DPT = D / 8;
-        if (n < R) {
-            float M = kNegInf;
+    if (w == 0) {
+        float mw[4], lw[4], sc[4];
+        mw[0] = m_run;
+        lw[0] = l_run;
 #pragma unroll
-            for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, mw[ww * 32 + n]);
-            float sc[4];
-            float W = 0.f;
+        for (int ww = 1; ww < 4; ++ww) {
+            mw[ww] = ml[((ww - 1) * 2 + 0) * 64 + lane];
+            lw[ww] = ml[((ww - 1) * 2 + 1) * 64 + lane];
+        }
+        float M = kNegInf;
 #pragma unroll
-            for (int ww = 0; ww < 4; ++ww) {
-                sc[ww] = M == kNegInf ? 0.f : fast_exp2(mw[ww * 32 + n] - M);
-                W += lw[ww * 32 + n] * sc[ww];
-            }
-            const float inv = W > 0.f ? 1.f / W : 0.f;
-            const int i = n / p.G, g = n % p.G;
-            const int64_t row = ((int64_t)b * p.Sq + i) * p.Hq + (int64_t)kvh * p.G + g;
+        for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, mw[ww]);
+        float L = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < 4; ++ww) {
+            sc[ww] = M == kNegInf ? 0.f : fast_exp2(mw[ww] - M);
+            L += lw[ww] * sc[ww];
+        }
+        L = xor32_sum(L);  // the two half-waves hold different keys of one query
+        const float inv = L > 0.f ? 1.f / L : 0.f;
+        if (cvalid) {
+            const int64_t row = ((int64_t)b * p.Sq + ci) * p.Hq + (int64_t)kvh * p.G + cg;
             const int64_t rows = (int64_t)p.B * p.Sq * p.Hq;
-            float* op = p.O_parts + ((int64_t)part * rows + row) * D + dg * DPT;
+            float* op = p.O_parts + ((int64_t)part * rows + row) * D;
 #pragma unroll
-            for (int e = 0; e < DPT; e += 4) {
-                float4 v;
-                float* vv = (float*)&v;
+            for (int db = 0; db < DB; ++db)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int dim = dg * DPT + e + q;
-                    float acc = 0.f;
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    float o[4];
 #pragma unroll
-                    for (int ww = 0; ww < 4; ++ww) acc += Ow[(ww * D + dim) * 32 + n] * sc[ww];
-                    vv[q] = acc * inv;
+                    for (int q = 0; q < 4; ++q) {
+                        const int r = 4 * g4 + q;
+                        float acc = oacc[db][r] * sc[0];
+#pragma unroll
+                        for (int ww = 1; ww < 4; ++ww) acc += Ow[((ww - 1) * DB * 16 + db * 16 + r) * 64 + lane] * sc[ww];
+                        o[q] = acc * inv;
+                    }
+                    // accumulator registers 4*g4..4*g4+3 hold dims db*32 + 8*g4 + 4h + 0..3
+                    *(float4*)(op + db * 32 + 8 * g4 + 4 * h) = make_float4(o[0], o[1], o[2], o[3]);
                 }
-                *(float4*)(op + e) = v;
-            }
-            if (dg == 0)
-                p.lse_parts[(int64_t)part * rows + row] = W > 0.f ? (M + __log2f(W)) * kLn2 : kNegInf;
+            if (h == 0)
+                p.lse_parts[(int64_t)part * rows + row] = L > 0.f ? (M + __log2f(L)) * kLn2 : kNegInf;
         }
     }
 }

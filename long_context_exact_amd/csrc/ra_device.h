@@ -17,6 +17,14 @@ constexpr float kNegInf = -__builtin_huge_valf();
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// MFMA row permutation for the QK^T product: swapping bits 2 and 3 of the
+// row index makes the 32x32 accumulator give each half-wave 8 consecutive
+// keys of every 16-key block (register r of half h <-> key 16*(r/8)+8h+r%8),
+// which is the layout of the B operand of the following PV product.
+__device__ __forceinline__ int swap_bits23(int m) {
+    return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
+}
+
 __device__ __forceinline__ float xor32_max(float x) { return fmaxf(x, __shfl_xor(x, 32, 64)); }
 __device__ __forceinline__ float xor32_sum(float x) { return x + __shfl_xor(x, 32, 64); }
 
