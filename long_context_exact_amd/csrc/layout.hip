@@ -6,9 +6,11 @@
 // natural position chunk(r, lc)*c + u with chunk(r, 0) = r and
 // chunk(r, 1) = 2P-1-r.  The contiguous split is the identity.
 //
-// Pure data movement: each thread copies 16-byte units (4- or 1-byte units
-// when a row is not a multiple of 16 bytes) of one destination row; the
-// source row is computed from the destination row.
+// Pure data movement.  Both splits move whole chunks of c rows, so the fast
+// kernel gives each work-group a contiguous byte range inside one chunk and
+// computes the source and destination chunk bases once (scalar arithmetic);
+// the threads then stream 16-byte units.  The general kernel (any alignment)
+// copies 16-, 4- or 1-byte units and maps every destination row to its source.
 #include "ra_device.h"
 
 namespace ra {
@@ -53,6 +55,44 @@ __global__ __launch_bounds__(256) void layout_kernel(LayoutArgs a) {
     }
 }
 
+// Chunk-level copy: work-group -> (outer index o, destination chunk q, byte
+// range of BYTES_PER_WG inside it).  Chunks are c rows of row_bytes.
+constexpr int64_t BYTES_PER_WG = 64 * 1024;
+
+struct ChunkArgs {
+    const uint8_t* src;
+    uint8_t* dst;
+    int64_t chunk_bytes, seq_bytes;  // one chunk; one outer slice (S rows)
+    int nchunks, wgs_per_chunk, P, zigzag, inverse;
+};
+
+__global__ __launch_bounds__(256) void layout_chunks_kernel(ChunkArgs a) {
+    const int part = (int)(blockIdx.x % (unsigned)a.wgs_per_chunk);
+    const unsigned rest = blockIdx.x / (unsigned)a.wgs_per_chunk;
+    const int q = (int)(rest % (unsigned)a.nchunks);
+    const int64_t o = rest / (unsigned)a.nchunks;
+    int sq = q;  // source chunk index
+    if (a.zigzag) {
+        if (!a.inverse) {
+            // destination sharded position q = 2r + lc holds natural chunk r or 2P-1-r
+            const int r = q >> 1, lc = q & 1;
+            sq = lc == 0 ? r : 2 * a.P - 1 - r;
+        } else {
+            // destination natural chunk q comes from sharded position 2r + lc
+            const int r = q < a.P ? q : 2 * a.P - 1 - q;
+            sq = 2 * r + (q < a.P ? 0 : 1);
+        }
+    }
+    const int64_t beg = (int64_t)part * BYTES_PER_WG;
+    int64_t len = a.chunk_bytes - beg;
+    if (len > BYTES_PER_WG) len = BYTES_PER_WG;
+    const uint4* s = (const uint4*)(a.src + o * a.seq_bytes + sq * a.chunk_bytes + beg);
+    uint4* d = (uint4*)(a.dst + o * a.seq_bytes + (int64_t)q * a.chunk_bytes + beg);
+    const int units = (int)(len >> 4);
+#pragma unroll 4
+    for (int i = threadIdx.x; i < units; i += 256) d[i] = s[i];
+}
+
 }  // namespace
 
 hipError_t launch_layout(const void* src, void* dst, int64_t outer, int64_t S, int64_t inner_bytes,
@@ -71,6 +111,24 @@ hipError_t launch_layout(const void* src, void* dst, int64_t outer, int64_t S, i
     const int64_t total_bytes = outer * S * inner_bytes;
     if (total_bytes <= 0) return hipSuccess;
     const uintptr_t align = (uintptr_t)src | (uintptr_t)dst;
+    {
+        ChunkArgs c;
+        c.chunk_bytes = a.c * inner_bytes;
+        c.seq_bytes = S * inner_bytes;
+        c.nchunks = zigzag ? 2 * P : P;
+        const int64_t wpc = (c.chunk_bytes + BYTES_PER_WG - 1) / BYTES_PER_WG;
+        const int64_t grid = outer * c.nchunks * wpc;
+        if (align % 16 == 0 && c.chunk_bytes % 16 == 0 && grid <= 0x7fffffffLL) {
+            c.src = (const uint8_t*)src;
+            c.dst = (uint8_t*)dst;
+            c.wgs_per_chunk = (int)wpc;
+            c.P = P;
+            c.zigzag = zigzag;
+            c.inverse = inverse;
+            hipLaunchKernelGGL(layout_chunks_kernel, dim3((unsigned)grid), dim3(256), 0, s, c);
+            return hipGetLastError();
+        }
+    }
     int64_t unit = 1;
     if (inner_bytes % 16 == 0 && align % 16 == 0)
         unit = 16;

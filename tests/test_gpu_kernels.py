@@ -193,6 +193,23 @@ def test_merge_kernel_vs_oracle(d, out):
     assert np.abs(l_g[fin] - l_ref[fin]).max() <= 1e-6 * max(1.0, np.abs(l_ref[fin]).max())
 
 
+@pytest.mark.parametrize("layout", ["contiguous", "zigzag"])
+def test_layout_gather_multi_range_chunks(layout):
+    """Chunks of 40 rows x 2 KiB (80 KiB) span two 64 KiB copy ranges, the
+    second one ragged; two outer slices."""
+    outer, S, P, inner = 2, 160, 2, 2048
+    rng = np.random.default_rng(1501)
+    x = rng.integers(0, 256, size=(outer, S, inner), dtype=np.uint8)
+    src = torch.from_numpy(x).cuda()
+    dst = torch.empty_like(src)
+    back = torch.empty_like(src)
+    ra.ra_layout_gather(src, dst, S, P, layout, inverse=False)
+    ra.ra_layout_gather(dst, back, S, P, layout, inverse=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(dst.cpu().numpy(), x[:, oracle.natural_positions(S, P, layout)])
+    assert np.array_equal(back.cpu().numpy(), x)
+
+
 @pytest.mark.parametrize("inner", [16, 4, 6, 256])
 @pytest.mark.parametrize("layout", ["contiguous", "zigzag"])
 def test_layout_gather_bit_exact(inner, layout):
