@@ -19,7 +19,7 @@ class Workload:
     d: int
     S: int             # prefill: sequence length; decode: KV length
     P: int             # ranks (prefill) or KV shards (decode)
-    layout: str        # "contiguous" | "zigzag" (prefill)
+    layout: str        # "contiguous" | "zigzag" | "zigzag<k>" | "striped" (prefill)
     causal: bool
     dtype: str         # "f32" | "bf16"
     Sq: int = 1        # decode queries per sequence
@@ -50,18 +50,49 @@ WORKLOADS = {
 }
 
 
+def layout_kind(layout: str) -> tuple[str, int]:
+    """"contiguous" -> (contiguous, 1); "zigzag" -> (zigzag, 2);
+    "zigzag<k>" -> (zigzag, k); "striped" -> (striped, 0)."""
+    if layout == "contiguous":
+        return "contiguous", 1
+    if layout == "zigzag":
+        return "zigzag", 2
+    if layout == "striped":
+        return "striped", 0
+    if layout.startswith("zigzag") and layout[6:].isdigit() and int(layout[6:]) >= 1:
+        return "zigzag", int(layout[6:])
+    raise ValueError(f"unknown layout {layout!r}")
+
+
 def causal_pairs_rank(S: int, P: int, layout: str, rank: int) -> int:
     """Closed-form count of unmasked (query, key) pairs of one rank under the
     global causal mask (used for FLOP accounting).
 
-    contiguous, n = S/P:  rank r scores r*n*n + n(n+1)/2 pairs;
-    zig-zag, c = S/(2P):  every rank scores 2P*c*c + c pairs.
+    contiguous, n = S/P:   rank r scores r*n*n + n(n+1)/2 pairs;
+    zig-zag, c = S/(2P):   every rank scores 2P*c*c + c pairs;
+    zig-zag with k chunks of c = S/(kP) tokens: a chunk with global id g
+                           scores c*c*g + c(c+1)/2 pairs, summed over the
+                           rank's chunks (even picks g = (i/2)P + r, odd
+                           picks g = kP-1-(i/2)P-r for local index i);
+    striped, n = S/P:      query j of rank r sits at r + jP, so the rank
+                           scores n(r+1) + P n(n-1)/2 pairs.
     """
-    if layout == "contiguous":
+    kind, k = layout_kind(layout)
+    if kind == "contiguous":
         n = S // P
         return rank * n * n + n * (n + 1) // 2
-    c = S // (2 * P)
-    return 2 * P * c * c + c
+    if kind == "striped":
+        n = S // P
+        return n * (rank + 1) + P * n * (n - 1) // 2
+    if k == 2:
+        c = S // (2 * P)
+        return 2 * P * c * c + c
+    c = S // (k * P)
+    total = 0
+    for i in range(k):
+        g = (i // 2) * P + rank if i % 2 == 0 else k * P - 1 - (i // 2) * P - rank
+        total += c * c * g + c * (c + 1) // 2
+    return total
 
 
 def prefill_flops(w: Workload, rank: int | None = None) -> int:

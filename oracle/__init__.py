@@ -84,22 +84,49 @@ def causal_chunk_workload(assign: dict[int, list[int]]) -> dict[int, int]:
     return {r: sum(q + 1 for q in qs) for r, qs in assign.items()}
 
 
-def local_chunks(layout: str, P: int, rank: int) -> list[int]:
-    """Global chunk ids a rank stores, in local order.
+def parse_layout(layout: str) -> tuple[str, int]:
+    """Layout name -> (kind, chunks per rank).
 
-    contiguous: P chunks of S/P tokens, rank r stores chunk r;
-    zigzag:     2P chunks of S/(2P) tokens, rank r stores [r, 2P-1-r].
+    "contiguous"      P chunks, one per rank (lesson 8, section 4A);
+    "zigzag"          2 chunks per rank, r and 2P-1-r (section 4B);
+    "zigzag<k>"       k chunks per rank by the exercise's general rule
+                      (``zigzag_assignment``), e.g. "zigzag4";
+    "striped"         tokens dealt round-robin: rank r holds positions
+                      r, r+P, r+2P, ... .  The pages only name striped
+                      attention as a rebalancing variant; this one-token
+                      stripe is the plain reading of the name.
+    For "striped" the chunk count is None (one token per chunk).
     """
     if layout == "contiguous":
-        return [rank]
+        return "contiguous", 1
     if layout == "zigzag":
-        return [rank, 2 * P - 1 - rank]
+        return "zigzag", 2
+    if layout.startswith("zigzag") and layout[6:].isdigit() and int(layout[6:]) >= 1:
+        return "zigzag", int(layout[6:])
+    if layout == "striped":
+        return "striped", None
+    raise ValueError(layout)
+
+
+def local_chunks(layout: str, P: int, rank: int) -> list[int]:
+    """Global chunk ids a rank stores, in local order (chunked layouts).
+
+    contiguous: P chunks of S/P tokens, rank r stores chunk r;
+    zigzag<k>:  kP chunks of S/(kP) tokens, rank r stores
+                ``zigzag_assignment(P, k)[r]`` ([r, 2P-1-r] for k = 2).
+    """
+    kind, k = parse_layout(layout)
+    if kind == "contiguous":
+        return [rank]
+    if kind == "zigzag":
+        return zigzag_assignment(P, k)[rank]
     raise ValueError(layout)
 
 
 def chunk_len(layout: str, S: int, P: int) -> int:
-    n_chunks = P if layout == "contiguous" else 2 * P
-    if S % n_chunks:
+    kind, k = parse_layout(layout)
+    n_chunks = S if kind == "striped" else P * k
+    if S % n_chunks or S % P:
         raise ValueError("sequence does not split evenly")
     return S // n_chunks
 
@@ -108,11 +135,14 @@ def natural_positions(S: int, P: int, layout: str) -> np.ndarray:
     """pos[k] = natural (global) position of row k of the rank-sharded order.
 
     Rank r's rows come after those of ranks 0..r-1; inside a rank the local
-    chunks follow ``local_chunks``.
+    chunks follow ``local_chunks`` (striped: the rank's positions in order).
     """
     c = chunk_len(layout, S, P)
     pos = []
     for r in range(P):
+        if parse_layout(layout)[0] == "striped":
+            pos.append(np.arange(r, S, P, dtype=np.int64))
+            continue
         for ch in local_chunks(layout, P, r):
             pos.append(np.arange(ch * c, (ch + 1) * c, dtype=np.int64))
     return np.concatenate(pos)

@@ -85,6 +85,11 @@ def test_exact_unmasked_pairs(P, S):
             assert oracle.unmasked_pairs(S, P, layout, r) == causal_pairs_rank(S, P, layout, r)
     tot = sum(oracle.unmasked_pairs(S, P, "zigzag", r) for r in range(P))
     assert tot == S * (S + 1) // 2
+    for layout in ("zigzag4", "striped"):
+        if S % (4 * P):
+            continue
+        for r in range(P):
+            assert oracle.unmasked_pairs(S, P, layout, r) == causal_pairs_rank(S, P, layout, r)
 
 
 def test_natural_positions_small():
@@ -94,6 +99,73 @@ def test_natural_positions_small():
     assert oracle.natural_positions(12, 3, "contiguous").tolist() == list(range(12))
     with pytest.raises(ValueError):
         oracle.natural_positions(10, 4, "zigzag")
+    # four chunks per rank, P = 2, chunks of 2: rank 0 holds chunks 0, 7, 2, 5
+    # and rank 1 holds 1, 6, 3, 4 (written out by hand from the rule)
+    assert oracle.natural_positions(16, 2, "zigzag4").tolist() == [
+        0, 1, 14, 15, 4, 5, 10, 11, 2, 3, 12, 13, 6, 7, 8, 9]
+    # token round-robin: rank r holds r, r+P, r+2P, ...
+    assert oracle.natural_positions(8, 2, "striped").tolist() == [0, 2, 4, 6, 1, 3, 5, 7]
+    assert oracle.natural_positions(9, 3, "striped").tolist() == [0, 3, 6, 1, 4, 7, 2, 5, 8]
+    with pytest.raises(ValueError):
+        oracle.natural_positions(10, 4, "striped")
+    with pytest.raises(ValueError):
+        oracle.natural_positions(16, 4, "zigzag3")
+    for bad in ("zigzag0", "zigzagx", "stripes", ""):
+        with pytest.raises(ValueError):
+            oracle.parse_layout(bad)
+
+
+LAYOUTS = ["contiguous", "zigzag", "zigzag3", "zigzag4", "zigzag6", "striped"]
+
+
+@pytest.mark.parametrize("P", [1, 2, 3, 4, 8])
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_layouts_are_permutations(layout, P):
+    # every layout deals every position to exactly one rank, S/P per rank
+    S = 48 * P
+    pos = oracle.natural_positions(S, P, layout)
+    assert sorted(pos.tolist()) == list(range(S))
+    n = S // P
+    if layout == "striped":
+        for r in range(P):
+            assert (pos[r * n:(r + 1) * n] % P == r).all()
+
+
+def test_zigzag_four_chunks_per_rank_explicit():
+    # the exercise's general rule for more than two chunks per rank, P = 4,
+    # k = 4, 16 chunks: even picks count forward from the front in rounds of
+    # P, odd picks count back from the end (written out by hand)
+    assert oracle.zigzag_assignment(4, 4) == {
+        0: [0, 15, 4, 11], 1: [1, 14, 5, 10], 2: [2, 13, 6, 9], 3: [3, 12, 7, 8]}
+    assert oracle.zigzag_assignment(3, 3) == {0: [0, 8, 3], 1: [1, 7, 4], 2: [2, 6, 5]}
+
+
+@pytest.mark.parametrize("P", list(range(1, 13)))
+def test_zigzag_even_k_balanced(P):
+    # an even pick q and its odd partner total-1-q sum to total-1, so with an
+    # even number of chunks per rank every rank does k/2 * (kP + 1) chunk pairs
+    for k in (2, 4, 6, 8):
+        w = oracle.causal_chunk_workload(oracle.zigzag_assignment(P, k))
+        assert set(w.values()) == {k // 2 * (k * P + 1)}
+    # an odd k leaves the last forward pick unpaired: unbalanced for P > 1
+    w3 = oracle.causal_chunk_workload(oracle.zigzag_assignment(P, 3))
+    assert (len(set(w3.values())) == 1) == (P == 1)
+
+
+@pytest.mark.parametrize("P,S", [(1, 6), (2, 8), (3, 9), (4, 40), (8, 64), (8, 8192)])
+def test_striped_unmasked_pairs_closed_form(P, S):
+    # rank r's j-th query sits at r + jP and sees r + jP + 1 keys:
+    # sum_j = n (r + 1) + P n (n - 1) / 2, n = S/P; all ranks sum to S(S+1)/2
+    n = S // P
+    tot = 0
+    for r in range(P):
+        got = oracle.unmasked_pairs(S, P, "striped", r)
+        assert got == n * (r + 1) + P * n * (n - 1) // 2
+        tot += got
+    assert tot == S * (S + 1) // 2
+    # ranks differ by exactly n pairs from one to the next
+    assert oracle.unmasked_pairs(S, P, "striped", P - 1) - oracle.unmasked_pairs(
+        S, P, "striped", 0) == n * (P - 1)
 
 
 # ------------------------------------------------------ attention definition
@@ -261,10 +333,10 @@ def test_online_fold_equals_definition_in_every_order(P, causal):
         np.testing.assert_allclose(lf, lse[0, 0, :], rtol=0, atol=1e-12)
 
 
-@pytest.mark.parametrize("layout", ["contiguous", "zigzag"])
+@pytest.mark.parametrize("layout", ["contiguous", "zigzag", "zigzag3", "zigzag4", "striped"])
 def test_ring_fold_per_rank_p8(layout):
     # each rank keeps its own query rows and folds the P shards in ring order
-    P, S, d = 8, 64, 16
+    P, S, d = 8, 96, 16
     Q = _rand((1, S, 1, d), (19,), "bf16")
     K = _rand((1, S, 1, d), (20,), "bf16")
     V = _rand((1, S, 1, d), (21,), "bf16")
@@ -430,3 +502,19 @@ def test_planted_fold_mistake_fails():
         o = o * (l / ln)[:, None] + p / ln[:, None] @ v[s0:s0 + S // P]   # missing exp(m - m~)
         m, l = mn, ln
     assert np.abs(o - O[0, :, 0]).max() > 1e-6
+
+
+def test_planted_layout_mistakes_fail_a_pin():
+    # odd picks counted from the wrong end / with the rank's sign flipped
+    def mutant(P, k, sign):
+        total = P * k
+        return {r: [(i // 2) * P + r if i % 2 == 0 else total - 1 - (i // 2) * P + sign * r
+                    for i in range(k)] for r in range(P)}
+    good = oracle.zigzag_assignment(4, 4)
+    assert mutant(4, 4, -1) == good
+    assert mutant(4, 4, +1) != good
+    # a striped split read as contiguous blocks breaks the striped closed form
+    S, P = 64, 4
+    n = S // P
+    contiguous_as_striped = [sum(range(r * n + 1, (r + 1) * n + 1)) for r in range(P)]
+    assert contiguous_as_striped != [n * (r + 1) + P * n * (n - 1) // 2 for r in range(P)]
