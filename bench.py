@@ -18,10 +18,15 @@ FLOPs, 4*d per scored (query, key) pair and head) as ``value``, with its
 roofline against the dense bf16 MFMA peak, and the decode path's HBM GB/s in
 the ``decode`` object.  ``cpu_baseline`` times the fp64 CPU oracle on a sample
 of the same prefill workload.
+
+--layout runs the same prefill shape under another split (contiguous,
+striped, zigzag<k>); --all-ranks adds the time of every rank's share, whose
+maximum is the length of one ring step when the ranks run side by side.
 """
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -67,9 +72,10 @@ def measured_traffic(kernel: str, files):
 
 def cpu_baseline(w, rank: int, n_rows: int):
     """The fp64 oracle on a bounded sample of the prefill workload: n_rows
-    query rows of ``rank`` (half from each of its two zig-zag chunks, evenly
-    spaced), every query head, each row scored against all the keys it may
-    see.  Returns TFLOP/s in the same FLOP convention as the GPU figure."""
+    query rows of ``rank``, evenly spaced over its local rows (under the
+    zig-zag split half from each of its two chunks), every query head, each
+    row scored against all the keys it may see.  Returns TFLOP/s in the same
+    FLOP convention as the GPU figure."""
     import numpy as np
 
     import oracle
@@ -78,19 +84,17 @@ def cpu_baseline(w, rank: int, n_rows: int):
     Q = synthetic.normal_tensor(w.q_shape, w.seed(0), "bf16")
     K = synthetic.normal_tensor(w.kv_shape, w.seed(1), "bf16")
     V = synthetic.normal_tensor(w.kv_shape, w.seed(2), "bf16")
-    c = w.S // (2 * w.P)
-    rows = []
-    for ch in (rank, 2 * w.P - 1 - rank):
-        rows += list(np.linspace(ch * c, (ch + 1) * c - 1, n_rows // 2).astype(np.int64))
-    rows = np.asarray(rows, dtype=np.int64)
+    n = w.S // w.P
+    mine = oracle.natural_positions(w.S, w.P, w.layout)[rank * n:(rank + 1) * n]
+    rows = mine[np.linspace(0, n - 1, n_rows).astype(np.int64)]
     flops = 4 * w.d * w.Hq * int(np.sum(rows + 1))
     t0 = time.perf_counter()
     oracle.attention_rows(Q, K, V, True, np.zeros_like(rows), rows)
     dt = time.perf_counter() - t0
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
             "kind": "oracle",
-            "sample": f"{len(rows)} query rows of rank {rank} (half from each of its two chunks), "
-                      f"all {w.Hq} heads, {flops / 1e9:.1f} GFLOP, {dt:.1f} s wall"}
+            "sample": f"{len(rows)} query rows of rank {rank} evenly spaced over its {w.layout} "
+                      f"rows, all {w.Hq} heads, {flops / 1e9:.1f} GFLOP, {dt:.1f} s wall"}
 
 
 def main() -> int:
@@ -102,6 +106,12 @@ def main() -> int:
     ap.add_argument("--decode-parts", type=int, default=64)
     ap.add_argument("--cpu-rows", type=int, default=128)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--all-ranks", action="store_true",
+                    help="also time every rank's share of the prefill (the ring step lasts as "
+                         "long as the slowest rank)")
+    ap.add_argument("--layout", default=None,
+                    help="prefill split: the workload's own (zig-zag, default) or another one "
+                         "(contiguous, striped, zigzag<k>) on the same shape")
     ap.add_argument("--workload", choices=["all", "prefill", "decode", "copy"], default="all",
                     help="copy: a plain 1 GiB device copy through the layout kernel (contiguous "
                          "layout), used to calibrate the HBM byte counters")
@@ -142,6 +152,9 @@ def main() -> int:
                           "ms": ms, "GB/s": 2 * nbytes / (ms * 1e-3) / 1e9}), flush=True)
         return 0
     wp, wd = WORKLOADS[4], WORKLOADS[5]
+    own_layout = args.layout is None or args.layout == wp.layout
+    if not own_layout:
+        wp = dataclasses.replace(wp, layout=args.layout)
 
     launches = []  # (stage, fn)
     if do_pre:
@@ -158,10 +171,10 @@ def main() -> int:
 
         def layout():
             for a, b in ((Qn, Qs), (Kn, Ks), (Vn, Vs)):
-                ra.ra_layout_gather(a, b, wp.S, wp.P, "zigzag", inverse=False)
+                ra.ra_layout_gather(a, b, wp.S, wp.P, wp.layout, inverse=False)
 
         def prefill():
-            ra.ra_fwd_rank(Q_r, Ks, Vs, O_r, L_r, wp.P, r, True, "zigzag")
+            ra.ra_fwd_rank(Q_r, Ks, Vs, O_r, L_r, wp.P, r, True, wp.layout)
 
         launches += [("layout", layout), ("prefill", prefill)]
     if do_dec:
@@ -222,7 +235,8 @@ def main() -> int:
         out.update({"value": tflops, "unit": "TFLOP/s"})
         out["roofline"] = {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS,
                            "unit": "TFLOP/s", "frac": tflops / PEAK_BF16_TFLOPS,
-                           "traffic": measured_traffic("prefill", PREFILL_SOURCES),
+                           "traffic": (measured_traffic("prefill", PREFILL_SOURCES)
+                                       if own_layout else None),
                            "kernel": "fwd_bf16_kernel<128>", "flops_per_launch": flops,
                            "ms_per_launch": ms["prefill"]}
         out["layout"] = {"value": lay_bytes / (ms["layout"] * 1e-3) / 1e9, "unit": "GB/s",
@@ -230,7 +244,7 @@ def main() -> int:
                          "frac_hbm": lay_bytes / (ms["layout"] * 1e-3) / 1e9 / PEAK_HBM_GBS}
         cfg.update({"workload": f"{wp.name} rank-{args.rank} share", "global_batch": wp.B,
                     "seq_len": wp.S, "heads_q": wp.Hq, "heads_kv": wp.Hkv, "head_dim": wp.d,
-                    "ranks": wp.P, "layout": "zigzag", "causal": True})
+                    "ranks": wp.P, "layout": wp.layout, "causal": True})
     if do_dec:
         nb = decode_bytes(wd, args.decode_parts)
         gbs = nb["attn_partial"] / (ms["decode"] * 1e-3) / 1e9
@@ -250,6 +264,25 @@ def main() -> int:
             cfg["workload"] = wd.name
     cfg["parallelism"] = "simulated ring (8 ranks resident on 1 GPU)"
     out["config"] = cfg
+    if do_pre and args.all_ranks:
+        log(f"timing each of the {wp.P} ranks, {args.steps} launches each")
+        per = []
+        for rr in range(wp.P):
+            Qrr = Qs[:, rr * n:(rr + 1) * n]
+            for _ in range(args.warmup):
+                ra.ra_fwd_rank(Qrr, Ks, Vs, O_r, L_r, wp.P, rr, True, wp.layout)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(args.steps):
+                ra.ra_fwd_rank(Qrr, Ks, Vs, O_r, L_r, wp.P, rr, True, wp.layout)
+            e1.record()
+            torch.cuda.synchronize()
+            per.append(e0.elapsed_time(e1) / args.steps)
+        total = prefill_flops(wp)
+        out["ranks"] = {"ms": [round(x, 4) for x in per], "ring_step_ms": max(per),
+                        "max_over_min": max(per) / min(per),
+                        "gflop": [round(prefill_flops(wp, rr) / 1e9, 1) for rr in range(wp.P)],
+                        "tflops_per_gpu_at_ring_step": total / wp.P / (max(per) * 1e-3) / 1e12}
     if do_pre and not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on {args.cpu_rows} sampled rows")
         out["cpu_baseline"] = cpu_baseline(wp, args.rank, args.cpu_rows)

@@ -13,10 +13,12 @@
  *         section 2 (ring loop: Q_r stays, K/V move r -> r+1, at step t rank r
  *         holds the block from (r - t) mod P), section 3 (online softmax
  *         update of (m, l, O)), section 4 (causal mask j <= i; naive split and
- *         the zig-zag split where rank r holds chunks r and 2P-1-r).
+ *         the zig-zag split where rank r holds chunks r and 2P-1-r) and the
+ *         exercise (the zig-zag rule for more than two chunks per rank).
  *   [P1]  "Paralelismo de sequencia e atencao de anel", aiunderstanding.org:
  *         every query ends up seeing every key; the result equals full
- *         attention.
+ *         attention; striped attention is named as another way to balance
+ *         the causal work (not defined there).
  *   [HX]  "NVIDIA Helix Parallelism" article, storagereview.com, phase 1: the
  *         KV cache is split along the sequence across devices, each computes a
  *         partial result, and one exchange combines them.
@@ -66,8 +68,17 @@ typedef enum {
 
 typedef enum {
     RA_LAYOUT_CONTIGUOUS = 0, /* P shards of S/P tokens; shard r = tokens [r*S/P, (r+1)*S/P) */
-    RA_LAYOUT_ZIGZAG = 1      /* 2P chunks of S/(2P) tokens; shard r = [chunk r ; chunk 2P-1-r] */
+    RA_LAYOUT_ZIGZAG = 1,     /* 2P chunks of S/(2P) tokens; shard r = [chunk r ; chunk 2P-1-r] */
+    RA_LAYOUT_STRIPED = 2     /* tokens dealt round-robin; shard r = positions r, r+P, r+2P, ... */
 } ra_layout;
+
+/* Zig-zag with k chunks per rank, 1 <= k <= RA_MAX_CHUNKS_PER_RANK: kP chunks
+ * of S/(kP) tokens; shard r = [chunk g(r,0) ; ... ; chunk g(r,k-1)] with
+ * g(r, i) = (i/2)P + r for even i and kP-1-(i/2)P-r for odd i ([L8] exercise).
+ * RA_LAYOUT_ZIGZAG_K(1) is the contiguous split, RA_LAYOUT_ZIGZAG_K(2) the
+ * usual zig-zag. */
+#define RA_LAYOUT_ZIGZAG_K(k) (0x100 | (k))
+#define RA_MAX_CHUNKS_PER_RANK 64
 
 typedef enum { RA_DTYPE_F32 = 0, RA_DTYPE_BF16 = 1 } ra_dtype;
 
@@ -76,8 +87,12 @@ typedef enum { RA_DTYPE_F32 = 0, RA_DTYPE_BF16 = 1 } ra_dtype;
  * shard 0's tokens, then shard 1's, ... (each shard S/P tokens).  Under
  * RA_LAYOUT_CONTIGUOUS this is the natural order.  Under RA_LAYOUT_ZIGZAG
  * shard r holds chunk r followed by chunk 2P-1-r ([L8] section 4B and the
- * exercise's answer, which lists the chunks in that order).  The causal mask
- * always compares natural (global) positions ([L8] section 4).
+ * exercise's answer, which lists the chunks in that order); under
+ * RA_LAYOUT_ZIGZAG_K(k) its k chunks in the order g(r, 0..k-1).  Under
+ * RA_LAYOUT_STRIPED shard r holds positions r, r+P, ..., S-P+r in ascending
+ * order ([P1] only names striped attention; dealing single tokens
+ * round-robin is this library's reading).  The causal mask always compares
+ * natural (global) positions ([L8] section 4).
  */
 
 /*
@@ -92,7 +107,8 @@ typedef enum { RA_DTYPE_F32 = 0, RA_DTYPE_BF16 = 1 } ra_dtype;
  *   O_r   [B, S/P, Hq, d]   output in o_dtype
  *   LSE_r [B, Hq, S/P]      fp32 output
  *   causal: 0 or 1; layout: ra_layout; dtype, o_dtype: ra_dtype.
- * Requirements: S % P == 0 (contiguous) or S % (2P) == 0 (zig-zag);
+ * Requirements: S % P == 0 (contiguous, striped), S % (2P) == 0 (zig-zag),
+ * S % (kP) == 0 (RA_LAYOUT_ZIGZAG_K(k)); S < 2^30 for bf16; P <= 4096;
  * 0 <= rank < P; Hq % Hkv == 0; d in {64, 128}.  Q_r/O_r must not alias K/V.
  * For B == 1, Q_r/O_r may point at rows rank*S/P of full sharded tensors.
  * The rows written are bit-identical to the same rows of ra_fwd_all.
@@ -145,13 +161,15 @@ int ra_attn_partial(const void* Q, const void* K, const void* V, float* O_parts,
 
 /*
  * ra_layout_gather -- move a sequence tensor between natural order and
- * sharded order ([L8] section 4B: the zig-zag chunk map).
+ * sharded order ([L8] section 4B and exercise: the zig-zag chunk maps; the
+ * striped token map).
  *   src, dst  [outer, S, inner_bytes] viewed as bytes; must not overlap.
  *   inverse = 0: natural -> sharded; inverse = 1: sharded -> natural.
  *   layout RA_LAYOUT_CONTIGUOUS is the identity (a copy).
  * Use outer = B and inner_bytes = H*d*elem for Q/K/V/O, and outer = B*Hq,
  * inner_bytes = 4 for an LSE array [B, Hq, S].
- * Requirements: S % (2P) == 0 for zig-zag, inner_bytes >= 1.
+ * Requirements: the split requirements of ra_fwd_rank (S < 2^31 for the
+ * striped split), inner_bytes >= 1.
  */
 int ra_layout_gather(const void* src, void* dst, int64_t outer, int64_t S,
                      int64_t inner_bytes, int P, int layout, int inverse, void* stream);

@@ -18,7 +18,13 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libra.so")
 
 RA_OK, RA_ERR_INVALID_ARG, RA_ERR_UNSUPPORTED, RA_ERR_HIP = 0, -1, -2, -3
-LAYOUTS = {"contiguous": 0, "zigzag": 1}
+LAYOUTS = {"contiguous": 0, "zigzag": 1, "striped": 2}
+MAX_CHUNKS_PER_RANK = 64
+
+
+def layout_zigzag_k(k: int) -> int:
+    """Code of the zig-zag split with k chunks per rank (RA_LAYOUT_ZIGZAG_K)."""
+    return 0x100 | int(k)
 DTYPE_F32, DTYPE_BF16 = 0, 1
 
 EXPORTS = ("ra_fwd_rank", "ra_fwd_all", "ra_merge_partials", "ra_attn_partial",
@@ -96,7 +102,15 @@ def _dev(t, name):
 
 
 def _layout(layout) -> int:
-    return LAYOUTS[layout] if isinstance(layout, str) else int(layout)
+    """"contiguous", "zigzag", "striped", "zigzag<k>" (e.g. "zigzag4") or an
+    integer code; unknown names raise, unknown codes are left to the library."""
+    if not isinstance(layout, str):
+        return int(layout)
+    if layout in LAYOUTS:
+        return LAYOUTS[layout]
+    if layout.startswith("zigzag") and layout[6:].isdigit():
+        return layout_zigzag_k(int(layout[6:]))
+    raise ValueError(f"unknown layout {layout!r}")
 
 
 def ra_fwd_rank(Q_r, K, V, O_r, LSE_r, P: int, rank: int, causal: bool, layout, stream=None):

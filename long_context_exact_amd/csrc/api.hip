@@ -30,6 +30,34 @@ int hip_status(hipError_t e, const char* what) {
     return ok();
 }
 
+// Layout code -> chunks per rank k and the striped flag; checks that S splits.
+struct Split {
+    int k;        // chunks per rank (1 for the contiguous and the striped split)
+    int striped;  // 1: token round-robin
+};
+
+int check_split(int layout, int64_t S, int P, Split& sp) {
+    sp.k = 1;
+    sp.striped = 0;
+    if (layout == RA_LAYOUT_CONTIGUOUS) {
+    } else if (layout == RA_LAYOUT_ZIGZAG) {
+        sp.k = 2;
+    } else if (layout == RA_LAYOUT_STRIPED) {
+        sp.striped = 1;
+    } else if ((layout & ~0xff) == 0x100 && (layout & 0xff) >= 1 &&
+               (layout & 0xff) <= RA_MAX_CHUNKS_PER_RANK) {
+        sp.k = layout & 0xff;
+    } else {
+        return fail(RA_ERR_INVALID_ARG, "unknown layout %d", layout);
+    }
+    if (P > 4096) return fail(RA_ERR_UNSUPPORTED, "P=%d exceeds 4096", P);
+    const int64_t parts = (int64_t)sp.k * P;
+    if (S % parts != 0)
+        return fail(RA_ERR_UNSUPPORTED, "S=%lld does not split into %lld equal chunks", (long long)S,
+                    (long long)parts);
+    return RA_OK;
+}
+
 // Checks shared by ra_fwd_rank and ra_fwd_all.
 int check_fwd(const void* Q, const void* K, const void* V, const void* O, const float* LSE, int B,
               int Hq, int Hkv, int64_t S, int d, int P, int causal, int layout, int dtype,
@@ -39,8 +67,9 @@ int check_fwd(const void* Q, const void* K, const void* V, const void* O, const 
         return fail(RA_ERR_INVALID_ARG, "sizes must be positive (B=%d Hq=%d Hkv=%d S=%lld P=%d)", B,
                     Hq, Hkv, (long long)S, P);
     if (causal != 0 && causal != 1) return fail(RA_ERR_INVALID_ARG, "causal must be 0 or 1");
-    if (layout != RA_LAYOUT_CONTIGUOUS && layout != RA_LAYOUT_ZIGZAG)
-        return fail(RA_ERR_INVALID_ARG, "unknown layout %d", layout);
+    Split sp;
+    const int rc = check_split(layout, S, P, sp);
+    if (rc != RA_OK) return rc;
     if (dtype != RA_DTYPE_F32 && dtype != RA_DTYPE_BF16)
         return fail(RA_ERR_INVALID_ARG, "unknown dtype %d", dtype);
     if (o_dtype != RA_DTYPE_F32 && o_dtype != RA_DTYPE_BF16)
@@ -49,12 +78,9 @@ int check_fwd(const void* Q, const void* K, const void* V, const void* O, const 
         return fail(RA_ERR_UNSUPPORTED, "fp32 inputs need an fp32 output");
     if (d != 64 && d != 128) return fail(RA_ERR_UNSUPPORTED, "head dim %d (supported: 64, 128)", d);
     if (Hq % Hkv != 0) return fail(RA_ERR_UNSUPPORTED, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
-    if (layout == RA_LAYOUT_CONTIGUOUS && S % P != 0)
-        return fail(RA_ERR_UNSUPPORTED, "S=%lld does not split into P=%d equal shards", (long long)S, P);
-    if (layout == RA_LAYOUT_ZIGZAG && S % (2 * (int64_t)P) != 0)
-        return fail(RA_ERR_UNSUPPORTED, "S=%lld does not split into 2P=%d equal chunks", (long long)S,
-                    2 * P);
-    if (P > 4096) return fail(RA_ERR_UNSUPPORTED, "P=%d exceeds 4096", P);
+    if (dtype == RA_DTYPE_BF16 && S >= (int64_t(1) << 30))
+        return fail(RA_ERR_UNSUPPORTED, "S=%lld: the bf16 kernel keeps positions in 31 bits",
+                    (long long)S);
     return RA_OK;
 }
 
@@ -68,9 +94,12 @@ ra::FwdParams plan_fwd(const void* Q, const void* K, const void* V, void* O, flo
     p.O = O;
     p.LSE = LSE;
     p.S = S;
+    Split sp;
+    check_split(layout, S, P, sp);  // validated by check_fwd
     p.n = S / P;
-    p.zigzag = layout == RA_LAYOUT_ZIGZAG;
-    p.c = p.zigzag ? p.n / 2 : p.n;
+    p.striped = sp.striped;
+    p.chunks_per_rank = sp.k;
+    p.c = p.n / sp.k;
     p.q_rows = q_local ? p.n : S;
     p.B = B;
     p.Hq = Hq;
@@ -84,7 +113,6 @@ ra::FwdParams plan_fwd(const void* Q, const void* K, const void* V, void* O, flo
     p.q_local = q_local;
     const int bm = dtype == RA_DTYPE_BF16 ? ra::FWD_BF16_BLOCK_M : ra::FWD_F32_BLOCK_M;
     p.tiles_per_chunk = (int)((p.c + bm - 1) / bm);
-    p.chunks_per_rank = p.zigzag ? 2 : 1;
     const int pairs = B * Hkv;
     p.xcd_pairs = (pairs % 8 == 0) ? pairs / 8 : 0;
     p.scale = (float)(1.0 / sqrt((double)d));
@@ -188,20 +216,19 @@ int ra_layout_gather(const void* src, void* dst, int64_t outer, int64_t S, int64
     if (!src || !dst) return fail(RA_ERR_INVALID_ARG, "null tensor pointer");
     if (outer <= 0 || S <= 0 || inner_bytes <= 0 || P <= 0)
         return fail(RA_ERR_INVALID_ARG, "sizes must be positive");
-    if (layout != RA_LAYOUT_CONTIGUOUS && layout != RA_LAYOUT_ZIGZAG)
-        return fail(RA_ERR_INVALID_ARG, "unknown layout %d", layout);
+    Split sp;
+    const int rc = check_split(layout, S, P, sp);
+    if (rc != RA_OK) return rc;
     if (inverse != 0 && inverse != 1) return fail(RA_ERR_INVALID_ARG, "inverse must be 0 or 1");
-    if (layout == RA_LAYOUT_ZIGZAG && S % (2 * (int64_t)P) != 0)
-        return fail(RA_ERR_UNSUPPORTED, "S=%lld does not split into 2P=%d equal chunks", (long long)S,
-                    2 * P);
-    if (layout == RA_LAYOUT_CONTIGUOUS && S % P != 0)
-        return fail(RA_ERR_UNSUPPORTED, "S=%lld does not split into P=%d equal shards", (long long)S, P);
+    if (sp.striped && S >= (int64_t(1) << 31))
+        return fail(RA_ERR_UNSUPPORTED, "S=%lld: the striped gather keeps rows in 32 bits",
+                    (long long)S);
     const uint8_t* s0 = (const uint8_t*)src;
     const uint8_t* d0 = (const uint8_t*)dst;
     const int64_t bytes = outer * S * inner_bytes;
     if (s0 < d0 + bytes && d0 < s0 + bytes) return fail(RA_ERR_INVALID_ARG, "src and dst overlap");
-    return hip_status(ra::launch_layout(src, dst, outer, S, inner_bytes, P,
-                                        layout == RA_LAYOUT_ZIGZAG, inverse, (hipStream_t)stream),
+    return hip_status(ra::launch_layout(src, dst, outer, S, inner_bytes, P, sp.k, sp.striped,
+                                        inverse, (hipStream_t)stream),
                       "layout kernel launch");
 }
 

@@ -179,7 +179,7 @@ __device__ __forceinline__ bool halves_any(bool b) {
 // Key-tile cursor, in ring order: step t = 0..P-1 visits shard (rank - t) mod
 // P (K/V travel r -> r+1, lesson 8 section 2), its chunks in local order and
 // each chunk's tiles in ascending order; under the causal mask only the
-// prefix of a chunk up to the tile's last query position is visited.  The
+// prefix of a chunk up to the tile's last query coordinate is visited.  The
 // same order as the generic iterator of the other kernels, in 32-bit fields
 // (positions < 2^30): advancing inside a segment is three adds, the segment
 // walk runs only at its end.  All fields are uniform across the work-group.
@@ -188,7 +188,7 @@ struct KvCur {
     int t, lc;   // ring step and local chunk of the current segment
     int tl;      // tiles of the segment after the current one
     int krow;    // first K/V row (sharded order) of the current tile
-    int kpos;    // global position of that row
+    int kpos;    // mask coordinate of that row (global position when chunked)
     int cleft;   // rows of the chunk from that row on
 };
 
@@ -196,9 +196,8 @@ __device__ __forceinline__ bool cur_seg(const FwdParams& p, int rank, int qmax, 
     int s = rank - c.t;
     if (s < 0) s += p.P;
     const int cl = (int)p.c;
-    const int gch = c.lc ? 2 * p.P - 1 - s : s;  // lc = 1 only for the zig-zag split
     c.krow = s * (int)p.n + c.lc * cl;
-    c.kpos = gch * cl;
+    c.kpos = p.striped ? (int)(s > rank) : global_chunk(p.P, p.chunks_per_rank, s, c.lc) * cl;
     int vis = cl;
     if (p.causal) vis = min(max(qmax - c.kpos + 1, 0), cl);
     c.tl = (vis + BN - 1) / BN - 1;
@@ -362,7 +361,6 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdParams p) {
     // S^T accumulators alternate, so consecutive MFMAs are independent.  Lane
     // (h, m) reads row 32*(j%2) + swap(m), 16-byte chunk 2*(j/2) + h, stored
     // at chunk (2*(j/2) + h) ^ (row mod KCH) = 2*(j/2) ^ (h ^ (swap(m) mod KCH)).
-    typedef __attribute__((address_space(3))) const char lds_char;
     const int sm = swap_bits23(m);
     uint32_t kbase = lds_addr(ldsK) + (uint32_t)(sm * 2 * D + 16 * (h ^ (sm & (T::KCH - 1))));
     // V operand j: keys 16*(j/DB).., dims 32*(j%DB)..; lane l of 16-lane group

@@ -1,15 +1,18 @@
 // layout.hip -- natural <-> rank-sharded sequence order.
 //
-// Lesson 8 "Context Parallelism (CP)", section 4B: with 2P chunks of S/(2P)
-// tokens, rank r holds chunks r and 2P-1-r (in that local order, as the
-// exercise's answer lists them).  Sharded row k = r*(S/P) + lc*c + u holds
-// natural position chunk(r, lc)*c + u with chunk(r, 0) = r and
-// chunk(r, 1) = 2P-1-r.  The contiguous split is the identity.
+// Lesson 8 "Context Parallelism (CP)", section 4B and the exercise: with k
+// chunks of c = S/(kP) tokens per rank, sharded row r*(S/P) + lc*c + u holds
+// natural position g(r, lc)*c + u, where g is the zig-zag chunk map (even
+// local chunks picked from the front, odd ones from the back; k = 2 gives
+// chunks r and 2P-1-r, k = 1 the identity).  Under the striped split
+// sharded row r*(S/P) + i holds natural position r + iP.
 //
-// Pure data movement.  Both splits move whole chunks of c rows, so the fast
-// kernel gives each work-group a contiguous byte range inside one chunk and
-// computes the source and destination chunk bases once (scalar arithmetic);
-// the threads then stream 16-byte units.  The general kernel (any alignment)
+// Pure data movement.  The chunked splits move whole chunks of c rows, so the
+// chunk kernel gives each work-group a contiguous byte range inside one chunk
+// and computes the source and destination chunk bases once (scalar
+// arithmetic); the threads then stream 16-byte units.  The striped split
+// moves single rows: the row kernel gives each wave whole rows and maps each
+// destination row to its source once.  The general kernel (any alignment)
 // copies 16-, 4- or 1-byte units and maps every destination row to its source.
 #include "ra_device.h"
 
@@ -21,22 +24,28 @@ struct LayoutArgs {
     uint8_t* dst;
     int64_t outer, S, row_bytes;
     int64_t n, c;  // tokens per shard, tokens per chunk
-    int P, zigzag, inverse;
+    int P, k, striped, inverse;
 };
 
+// natural chunk of the sharded chunk slot q = rank * k + lc, and back
+__device__ __forceinline__ int64_t natural_chunk(int P, int k, int64_t q) {
+    return global_chunk(P, k, (int)(q / k), (int)(q % k));
+}
+__device__ __forceinline__ int64_t sharded_slot(int P, int k, int64_t g) {
+    const int band = (int)(g / P);
+    const int lc = band_chunk(k, band);
+    const int64_t rank = (lc & 1) ? (int64_t)k * P - 1 - (int64_t)(lc >> 1) * P - g : g - (int64_t)band * P;
+    return rank * k + lc;
+}
+
 __device__ __forceinline__ int64_t src_row(const LayoutArgs& a, int64_t k) {
-    if (!a.zigzag) return k;
-    if (!a.inverse) {  // dst sharded row k <- src natural position
-        const int64_t r = k / a.n, local = k % a.n;
-        const int64_t lc = local / a.c, u = local % a.c;
-        const int64_t ch = lc == 0 ? r : 2 * a.P - 1 - r;
-        return ch * a.c + u;
+    if (a.striped) {
+        if (!a.inverse) return (k % a.n) * a.P + k / a.n;  // sharded row r*n + i <- r + iP
+        return (k % a.P) * a.n + k / a.P;                  // natural r + iP <- sharded r*n + i
     }
-    // dst natural position k <- src sharded row
-    const int64_t ch = k / a.c, u = k % a.c;
-    const int64_t r = ch < a.P ? ch : 2 * a.P - 1 - ch;
-    const int64_t lc = ch < a.P ? 0 : 1;
-    return r * a.n + lc * a.c + u;
+    const int64_t q = k / a.c, u = k % a.c;
+    if (!a.inverse) return natural_chunk(a.P, a.k, q) * a.c + u;
+    return sharded_slot(a.P, a.k, q) * a.c + u;
 }
 
 template <typename U>
@@ -63,7 +72,7 @@ struct ChunkArgs {
     const uint8_t* src;
     uint8_t* dst;
     int64_t chunk_bytes, seq_bytes;  // one chunk; one outer slice (S rows)
-    int nchunks, wgs_per_chunk, P, zigzag, inverse;
+    int nchunks, wgs_per_chunk, P, k, inverse;
 };
 
 __global__ __launch_bounds__(256) void layout_chunks_kernel(ChunkArgs a) {
@@ -71,18 +80,9 @@ __global__ __launch_bounds__(256) void layout_chunks_kernel(ChunkArgs a) {
     const unsigned rest = blockIdx.x / (unsigned)a.wgs_per_chunk;
     const int q = (int)(rest % (unsigned)a.nchunks);
     const int64_t o = rest / (unsigned)a.nchunks;
-    int sq = q;  // source chunk index
-    if (a.zigzag) {
-        if (!a.inverse) {
-            // destination sharded position q = 2r + lc holds natural chunk r or 2P-1-r
-            const int r = q >> 1, lc = q & 1;
-            sq = lc == 0 ? r : 2 * a.P - 1 - r;
-        } else {
-            // destination natural chunk q comes from sharded position 2r + lc
-            const int r = q < a.P ? q : 2 * a.P - 1 - q;
-            sq = 2 * r + (q < a.P ? 0 : 1);
-        }
-    }
+    // source chunk: destination slot q holds natural chunk g(q / k, q % k);
+    // destination natural chunk q comes from the slot that holds it
+    const int64_t sq = a.inverse ? sharded_slot(a.P, a.k, q) : natural_chunk(a.P, a.k, q);
     const int64_t beg = (int64_t)part * BYTES_PER_WG;
     int64_t len = a.chunk_bytes - beg;
     if (len > BYTES_PER_WG) len = BYTES_PER_WG;
@@ -93,10 +93,37 @@ __global__ __launch_bounds__(256) void layout_chunks_kernel(ChunkArgs a) {
     for (int i = threadIdx.x; i < units; i += 256) d[i] = s[i];
 }
 
+// Striped row copy: work-group -> (outer index o, ROWS consecutive
+// destination rows); wave w copies rows w, w+4, ... of them, 16 bytes a lane.
+struct RowArgs {
+    const uint8_t* src;
+    uint8_t* dst;
+    int64_t row_bytes, seq_bytes;
+    unsigned S, n, P;
+    int rows_per_wg, wgs_per_seq, inverse;
+};
+
+__global__ __launch_bounds__(256) void layout_rows_kernel(RowArgs a) {
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const unsigned blk = blockIdx.x % (unsigned)a.wgs_per_seq;
+    const int64_t o = blockIdx.x / (unsigned)a.wgs_per_seq;
+    const unsigned k0 = blk * (unsigned)a.rows_per_wg;
+    const int units = (int)(a.row_bytes >> 4);
+    for (int rr = w; rr < a.rows_per_wg; rr += 4) {
+        const unsigned k = k0 + (unsigned)rr;
+        if (k >= a.S) break;
+        const unsigned sk = a.inverse ? (k % a.P) * a.n + k / a.P : (k % a.n) * a.P + k / a.n;
+        const uint4* s = (const uint4*)(a.src + o * a.seq_bytes + (int64_t)sk * a.row_bytes);
+        uint4* d = (uint4*)(a.dst + o * a.seq_bytes + (int64_t)k * a.row_bytes);
+        for (int i = lane; i < units; i += 64) d[i] = s[i];
+    }
+}
+
 }  // namespace
 
 hipError_t launch_layout(const void* src, void* dst, int64_t outer, int64_t S, int64_t inner_bytes,
-                         int P, int zigzag, int inverse, hipStream_t s) {
+                         int P, int chunks_per_rank, int striped, int inverse, hipStream_t s) {
     LayoutArgs a;
     a.src = (const uint8_t*)src;
     a.dst = (uint8_t*)dst;
@@ -104,18 +131,40 @@ hipError_t launch_layout(const void* src, void* dst, int64_t outer, int64_t S, i
     a.S = S;
     a.row_bytes = inner_bytes;
     a.P = P;
-    a.zigzag = zigzag;
+    a.k = chunks_per_rank;
+    a.striped = striped;
     a.inverse = inverse;
     a.n = S / P;
-    a.c = zigzag ? S / (2 * P) : a.n;
+    a.c = a.n / chunks_per_rank;
     const int64_t total_bytes = outer * S * inner_bytes;
     if (total_bytes <= 0) return hipSuccess;
     const uintptr_t align = (uintptr_t)src | (uintptr_t)dst;
-    {
+    if (striped) {
+        RowArgs r;
+        // about 64 KiB per work-group, whole rows, at least one row per wave
+        int64_t rows = BYTES_PER_WG / inner_bytes;
+        rows = rows < 4 ? 4 : (rows > 256 ? 256 : rows);
+        const int64_t wps = (S + rows - 1) / rows;
+        const int64_t grid = outer * wps;
+        if (align % 16 == 0 && inner_bytes % 16 == 0 && inner_bytes >= 64 && grid <= 0x7fffffffLL) {
+            r.src = (const uint8_t*)src;
+            r.dst = (uint8_t*)dst;
+            r.row_bytes = inner_bytes;
+            r.seq_bytes = S * inner_bytes;
+            r.S = (unsigned)S;
+            r.n = (unsigned)a.n;
+            r.P = (unsigned)P;
+            r.rows_per_wg = (int)rows;
+            r.wgs_per_seq = (int)wps;
+            r.inverse = inverse;
+            hipLaunchKernelGGL(layout_rows_kernel, dim3((unsigned)grid), dim3(256), 0, s, r);
+            return hipGetLastError();
+        }
+    } else {
         ChunkArgs c;
         c.chunk_bytes = a.c * inner_bytes;
         c.seq_bytes = S * inner_bytes;
-        c.nchunks = zigzag ? 2 * P : P;
+        c.nchunks = chunks_per_rank * P;
         const int64_t wpc = (c.chunk_bytes + BYTES_PER_WG - 1) / BYTES_PER_WG;
         const int64_t grid = outer * c.nchunks * wpc;
         if (align % 16 == 0 && c.chunk_bytes % 16 == 0 && grid <= 0x7fffffffLL) {
@@ -123,7 +172,7 @@ hipError_t launch_layout(const void* src, void* dst, int64_t outer, int64_t S, i
             c.dst = (uint8_t*)dst;
             c.wgs_per_chunk = (int)wpc;
             c.P = P;
-            c.zigzag = zigzag;
+            c.k = chunks_per_rank;
             c.inverse = inverse;
             hipLaunchKernelGGL(layout_chunks_kernel, dim3((unsigned)grid), dim3(256), 0, s, c);
             return hipGetLastError();

@@ -29,27 +29,44 @@ __device__ __forceinline__ float xor32_max(float x) { return fmaxf(x, __shfl_xor
 __device__ __forceinline__ float xor32_sum(float x) { return x + __shfl_xor(x, 32, 64); }
 
 // ----------------------------------------------------------------------------
+// Chunk maps of the splits (lesson 8, section 4 and its exercise).
+//
+// With k chunks per rank and kP chunks in all, local chunk lc of rank r is
+// global chunk (lc/2) P + r for even lc (picked from the front, one round of
+// P per pair) and kP - 1 - (lc/2) P - r for odd lc (picked from the back).
+// k = 1 is the contiguous split and k = 2 the usual zig-zag {r, 2P-1-r}.
+// The global chunks fall into k bands of P consecutive ids; band b holds the
+// even picks lc = 2b for b < ceil(k/2) and the odd picks lc = 2(k-1-b)+1
+// above, so a global chunk maps back to (rank, lc) through its band.
+// ----------------------------------------------------------------------------
+__device__ __forceinline__ int global_chunk(int P, int k, int rank, int lc) {
+    const int j = lc >> 1;
+    return (lc & 1) ? k * P - 1 - j * P - rank : j * P + rank;
+}
+
+__device__ __forceinline__ int band_chunk(int k, int b) {
+    return b < (k + 1) / 2 ? 2 * b : 2 * (k - 1 - b) + 1;
+}
+
+// ----------------------------------------------------------------------------
 // Query tiles of one prefill launch.
 //
 // Work-group id -> (batch, query head, rank, local chunk, tile).  Tiles are
 // handed out heaviest first: under the causal mask the work of a query tile
-// grows with its global position, so tiles are enumerated by descending global
-// chunk and, inside a chunk, descending offset.  When the number of
-// (batch, kv head) pairs is a multiple of the 8 XCDs, work-group ids are
-// grouped so that all query heads reading one kv head run on one XCD (ids are
-// dispatched round-robin over the XCDs) and share its L2.
+// grows with its mask coordinate, so tiles are enumerated by descending
+// global chunk and, inside a chunk, descending offset (striped split: by
+// descending local offset, ranks interleaved, since every rank's tile at one
+// offset does the same work).  When the number of (batch, kv head) pairs is a
+// multiple of the 8 XCDs, work-group ids are grouped so that all query heads
+// reading one kv head run on one XCD (ids are dispatched round-robin over the
+// XCDs) and share its L2.
 // ----------------------------------------------------------------------------
 struct QTile {
     int b, qh, kvh, rank;
-    int64_t gchunk;  // global chunk id of the tile
     int64_t q_row0;  // first row in the Q/O tensors
-    int64_t pos0;    // global position of the first row
+    int64_t pos0;    // mask coordinate of the first row
     int rows;        // valid rows (<= BLOCK_M)
 };
-
-__device__ __forceinline__ int64_t global_chunk(const FwdParams& p, int rank, int lc) {
-    return lc == 0 ? (int64_t)rank : (int64_t)(2 * p.P - 1 - rank);
-}
 
 template <int BM>
 __device__ __forceinline__ QTile decode_qtile(const FwdParams& p, unsigned id) {
@@ -73,25 +90,32 @@ __device__ __forceinline__ QTile decode_qtile(const FwdParams& p, unsigned id) {
     t.kvh = pair % p.Hkv;
     t.qh = t.kvh * p.G + g;
     const int tpc = p.tiles_per_chunk;
-    const int cidx = trank / tpc;
-    const int j = tpc - 1 - (trank % tpc);
-    int rank, lc;
-    if (!p.zigzag) {
-        rank = p.rank_lo + p.n_ranks - 1 - cidx;
+    const int k = p.chunks_per_rank;
+    int rank, lc, j;
+    int64_t pos_chunk;
+    if (p.striped) {
+        j = tpc - 1 - trank / p.n_ranks;
+        rank = p.rank_lo + trank % p.n_ranks;
         lc = 0;
-    } else if (p.n_ranks == 1) {
-        rank = p.rank_lo;
-        lc = cidx == 0 ? 1 : 0;
+        pos_chunk = 0;
     } else {
-        const int gch = 2 * p.P - 1 - cidx;
-        rank = gch < p.P ? gch : 2 * p.P - 1 - gch;
-        lc = gch < p.P ? 0 : 1;
+        const int cidx = trank / tpc;
+        j = tpc - 1 - (trank % tpc);
+        if (p.n_ranks == 1) {
+            rank = p.rank_lo;
+            lc = band_chunk(k, k - 1 - cidx);
+        } else {
+            const int gch = k * p.P - 1 - cidx;
+            const int band = gch / p.P;
+            lc = band_chunk(k, band);
+            rank = (lc & 1) ? k * p.P - 1 - (lc >> 1) * p.P - gch : gch - band * p.P;
+        }
+        pos_chunk = (int64_t)global_chunk(p.P, k, rank, lc) * p.c;
     }
     t.rank = rank;
-    t.gchunk = p.zigzag ? global_chunk(p, rank, lc) : (int64_t)rank;
     const int64_t off = (int64_t)j * BM;
     t.q_row0 = (p.q_local ? 0 : (int64_t)rank * p.n) + (int64_t)lc * p.c + off;
-    t.pos0 = t.gchunk * p.c + off;
+    t.pos0 = pos_chunk + off;
     const int64_t left = p.c - off;
     t.rows = left < BM ? (int)left : BM;
     return t;
@@ -105,22 +129,23 @@ __device__ __forceinline__ QTile decode_qtile(const FwdParams& p, unsigned id) {
 // r - t).  Inside a shard the chunks are visited in local order and each
 // chunk's key tiles in ascending order.  Under the causal mask only the
 // prefix of a chunk whose positions do not exceed the tile's last query is
-// visited; tiles wholly in the future of every query of the tile are skipped.
+// visited (in mask coordinates); tiles wholly in the future of every query of
+// the tile are skipped.
 // All fields are uniform across the work-group.
 // ----------------------------------------------------------------------------
 struct KvIter {
     int t, lc, tile, ntiles;
     int64_t krow;  // first K/V row (sharded order) of the current chunk
-    int64_t kpos;  // global position of that row
+    int64_t kpos;  // mask coordinate of that row
 };
 
 __device__ __forceinline__ void kv_seg(const FwdParams& p, int rank, int64_t qmax, int bn,
                                        KvIter& it) {
     int s = rank - it.t;
     if (s < 0) s += p.P;
-    const int64_t gch = p.zigzag ? global_chunk(p, s, it.lc) : (int64_t)s;
     it.krow = (int64_t)s * p.n + (int64_t)it.lc * p.c;
-    it.kpos = gch * p.c;
+    it.kpos = p.striped ? (int64_t)(s > rank)
+                        : (int64_t)global_chunk(p.P, p.chunks_per_rank, s, it.lc) * p.c;
     int64_t vis = p.c;
     if (p.causal) {
         vis = qmax - it.kpos + 1;

@@ -10,9 +10,17 @@ namespace ra {
 // Which query tiles one prefill launch covers and how they are ordered.
 //
 // The queries of a rank are cut into tiles that never straddle a chunk (a
-// rank owns one chunk under the contiguous split and two under zig-zag), so
-// the global positions inside one query tile are consecutive.  Key tiles
-// likewise stay inside one chunk.
+// rank owns one chunk under the contiguous and the striped split and k under
+// zig-zag), so the mask coordinates inside one query tile are consecutive.
+// Key tiles likewise stay inside one chunk.
+//
+// Mask coordinates.  For the chunked splits the coordinate of a token is its
+// global position.  Under the striped split rank r holds positions r + iP,
+// i = 0..n-1, and a key of shard s at local index j is visible to the query
+// at local index i iff s + jP <= r + iP, i.e. j + (s > r) <= i: the query's
+// coordinate is i and the key's is j + (s > r).  Either way a key is visible
+// iff its coordinate does not exceed the query's, and coordinates advance by
+// one per row inside a chunk.
 struct FwdParams {
     const void* Q;     // [B, q_rows, Hq, d]
     const void* K;     // [B, S, Hkv, d], sharded order
@@ -21,18 +29,18 @@ struct FwdParams {
     float* LSE;        // [B, Hq, q_rows]
     int64_t S;         // total tokens (all shards)
     int64_t n;         // tokens per shard, S / P
-    int64_t c;         // tokens per chunk: n (contiguous) or n / 2 (zig-zag)
+    int64_t c;         // tokens per chunk: n / chunks_per_rank
     int64_t q_rows;    // rows of Q/O/LSE: S for all ranks, n for one rank
     int B, Hq, Hkv, G; // G = Hq / Hkv
     int P;
-    int zigzag;        // 0 contiguous, 1 zig-zag
+    int striped;       // 1: token round-robin split (one chunk per rank)
     int causal;
     int o_f32;         // 1: O is fp32, 0: O has the input dtype (bf16)
     int rank_lo;       // first rank of this launch
     int n_ranks;       // ranks in this launch (P for all, 1 for one rank)
     int q_local;       // 1: Q/O/LSE rows are rank-local (row 0 = first row of rank_lo)
     int tiles_per_chunk;   // ceil(c / BLOCK_M)
-    int chunks_per_rank;   // 1 or 2
+    int chunks_per_rank;   // k: 1 contiguous or striped, k >= 2 zig-zag
     int xcd_pairs;     // (b, kv head) pairs per XCD group, 0 = no XCD grouping
     float scale_log2;  // log2(e) / sqrt(d)
     float scale;       // 1 / sqrt(d)
@@ -69,7 +77,7 @@ hipError_t launch_decode_bf16(const DecodeParams& p, int d, hipStream_t s);
 hipError_t launch_decode_f32(const DecodeParams& p, int d, hipStream_t s);
 hipError_t launch_merge(const MergeParams& p, int d, hipStream_t s);
 hipError_t launch_layout(const void* src, void* dst, int64_t outer, int64_t S, int64_t inner_bytes,
-                         int P, int zigzag, int inverse, hipStream_t s);
+                         int P, int chunks_per_rank, int striped, int inverse, hipStream_t s);
 
 // Tile shapes of the prefill kernels (the host needs them for the grid).
 constexpr int FWD_BF16_BLOCK_M = 256;

@@ -96,7 +96,8 @@ def sample_rows(S: int, P: int, layout: str, per_rank: int, seed) -> np.ndarray:
     rng = np.random.default_rng(seed)
     pos = oracle.natural_positions(S, P, layout)
     n = S // P
-    c = oracle.chunk_len(layout, S, P)
+    # a striped rank's rows are one strided chunk
+    c = n if layout == "striped" else oracle.chunk_len(layout, S, P)
     rows = []
     for r in range(P):
         mine = pos[r * n:(r + 1) * n]

@@ -65,6 +65,13 @@ def _fwd_rank(**kw):
     (dict(Hq=12, Hkv=8), ra.RA_ERR_UNSUPPORTED),
     (dict(S=8200), ra.RA_ERR_UNSUPPORTED),                 # 8200 % 16 != 0 under zig-zag
     (dict(S=8200, layout=0), ra.RA_ERR_UNSUPPORTED),       # 8200 % 8 == 0 but zig-zag needs 2P
+    (dict(layout=3), ra.RA_ERR_INVALID_ARG),
+    (dict(layout=0x100), ra.RA_ERR_INVALID_ARG),           # zig-zag with 0 chunks per rank
+    (dict(layout=0x100 | 65), ra.RA_ERR_INVALID_ARG),      # above RA_MAX_CHUNKS_PER_RANK
+    (dict(layout=0x202), ra.RA_ERR_INVALID_ARG),
+    (dict(layout=0x104, S=8208), ra.RA_ERR_UNSUPPORTED),   # 8208 % 16 == 0, % 32 != 0
+    (dict(layout=2, S=8204), ra.RA_ERR_UNSUPPORTED),       # striped needs S % P == 0
+    (dict(layout=0, S=1 << 30), ra.RA_ERR_UNSUPPORTED),    # bf16 positions in 31 bits
 ])
 def test_fwd_rank_rejects(kw, code):
     if kw == dict(S=8200, layout=0):
@@ -77,7 +84,7 @@ def test_fwd_all_and_others_reject():
     L = ra.lib()
     assert L.ra_fwd_all(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 4, 4, 1000, 64, 3, 0, 0, 0, 0, NULL) \
         == ra.RA_ERR_UNSUPPORTED
-    assert "equal shards" in ra.last_error()
+    assert "equal chunks" in ra.last_error()
     assert L.ra_merge_partials(FAKE, FAKE, FAKE, NULL, 0, 10, 128, 1, NULL) == ra.RA_ERR_INVALID_ARG
     assert L.ra_merge_partials(FAKE, FAKE, FAKE, NULL, 2, 10, 80, 1, NULL) == ra.RA_ERR_UNSUPPORTED
     assert L.ra_merge_partials(NULL, FAKE, FAKE, NULL, 2, 10, 128, 1, NULL) == ra.RA_ERR_INVALID_ARG
@@ -89,6 +96,23 @@ def test_fwd_all_and_others_reject():
     assert L.ra_layout_gather(FAKE, FAKE, 1, 30, 16, 4, 1, 0, NULL) == ra.RA_ERR_UNSUPPORTED
     assert L.ra_layout_gather(FAKE, FAKE, 1, 32, 16, 4, 1, 0, NULL) == ra.RA_ERR_INVALID_ARG  # overlap
     assert L.ra_layout_gather(FAKE, FAKE, 1, 32, 16, 4, 1, 3, NULL) == ra.RA_ERR_INVALID_ARG
+    assert L.ra_layout_gather(FAKE, FAKE, 1, 32, 16, 4, 0x103, 0, NULL) == ra.RA_ERR_UNSUPPORTED
+    assert L.ra_layout_gather(FAKE, FAKE, 1, 30, 16, 4, 2, 0, NULL) == ra.RA_ERR_UNSUPPORTED
+    assert L.ra_layout_gather(FAKE, FAKE, 1, 32, 16, 4, 4, 0, NULL) == ra.RA_ERR_INVALID_ARG
+
+
+def test_binding_layout_names():
+    assert ra._layout("contiguous") == 0 and ra._layout("zigzag") == 1
+    assert ra._layout("striped") == 2
+    assert ra._layout("zigzag4") == 0x104 == ra.layout_zigzag_k(4)
+    assert ra._layout(0x103) == 0x103
+    for bad in ("zigzagx", "zig", "stripe"):
+        with pytest.raises(ValueError):
+            ra._layout(bad)
+    hdr = open(os.path.join(os.path.dirname(__file__), "..", "include", "ra.h")).read()
+    assert "#define RA_LAYOUT_ZIGZAG_K(k) (0x100 | (k))" in hdr
+    assert f"#define RA_MAX_CHUNKS_PER_RANK {ra.MAX_CHUNKS_PER_RANK}" in hdr
+    assert "RA_LAYOUT_STRIPED = 2" in hdr
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

@@ -5,6 +5,8 @@ Small workloads are checked on every output row; the 32k and 128k-token
 workloads on seeded sampled rows (per rank: the first and last row of each
 of its chunks plus random rows), every query head; the 1M-key decode on two
 whole sequences (all 64 heads)."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -29,9 +31,14 @@ def _bits(t):
     return t.view(torch.int16) if t.dtype == torch.bfloat16 else t
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
-def test_prefill_workload(cfg):
+@pytest.mark.parametrize("cfg,layout", [(1, None), (2, None), (3, None), (4, None),
+                                        (3, "zigzag4"), (3, "striped")])
+def test_prefill_workload(cfg, layout):
+    """layout: None for the workload's own split; otherwise the same inputs and
+    shape under another split (the causal rebalancing variants)."""
     w = WORKLOADS[cfg]
+    if layout is not None:
+        w = dataclasses.replace(w, layout=layout, name=f"{w.name}-as-{layout}")
     log(f"workload {cfg} {w.name}: generating inputs")
     Qn, Kn, Vn = _inputs(w)
     S, P, lay = w.S, w.P, w.layout

@@ -26,6 +26,17 @@ PREFILL = [  # B, S, Hq, Hkv, d, P, layout, causal, dtype
     (1, 300, 2, 2, 64, 1, "zigzag", True, "bf16"),      # one rank, two chunks
     (1, 512, 2, 2, 64, 16, "zigzag", True, "bf16"),     # chunks of 16
     (1, 4096, 8, 2, 128, 4, "zigzag", True, "bf16"),    # GQA, chunks of 512
+    # k chunks per rank and the striped split
+    (1, 768, 2, 2, 64, 4, "zigzag3", True, "f32"),      # chunks of 64
+    (1, 520, 2, 1, 64, 2, "striped", True, "f32"),      # shards of 260
+    (2, 1280, 4, 2, 128, 4, "zigzag4", True, "bf16"),   # chunks of 80
+    (1, 2304, 4, 4, 128, 8, "zigzag3", True, "bf16"),   # chunks of 96, unbalanced k
+    (1, 1040, 4, 2, 128, 4, "striped", True, "bf16"),   # shards of 260: ragged tiles
+    (1, 1536, 2, 2, 64, 3, "striped", False, "bf16"),
+    (1, 600, 2, 2, 128, 1, "zigzag6", True, "bf16"),    # one rank, six chunks of 100
+    (1, 512, 2, 2, 64, 1, "striped", True, "bf16"),     # one rank: the identity
+    (1, 4096, 8, 2, 128, 8, "striped", True, "bf16"),   # GQA
+    (1, 4096, 8, 2, 128, 4, "zigzag8", True, "bf16"),   # chunks of 128
 ]
 
 
@@ -86,7 +97,7 @@ STRESS = ["peaky", "late_max", "zero_q"]
 
 
 @pytest.mark.parametrize("kind", STRESS)
-@pytest.mark.parametrize("layout", ["contiguous", "zigzag"])
+@pytest.mark.parametrize("layout", ["contiguous", "zigzag", "zigzag4", "striped"])
 def test_prefill_stress_inputs(kind, layout):
     B, S, Hq, Hkv, d, P = 1, 1024, 4, 2, 128, 4
     log(f"stress {kind} {layout}")
@@ -193,7 +204,7 @@ def test_merge_kernel_vs_oracle(d, out):
     assert np.abs(l_g[fin] - l_ref[fin]).max() <= 1e-6 * max(1.0, np.abs(l_ref[fin]).max())
 
 
-@pytest.mark.parametrize("layout", ["contiguous", "zigzag"])
+@pytest.mark.parametrize("layout", ["contiguous", "zigzag", "zigzag4", "striped"])
 def test_layout_gather_multi_range_chunks(layout):
     """Chunks of 40 rows x 2 KiB (80 KiB) span two 64 KiB copy ranges, the
     second one ragged; two outer slices."""
@@ -210,8 +221,8 @@ def test_layout_gather_multi_range_chunks(layout):
     assert np.array_equal(back.cpu().numpy(), x)
 
 
-@pytest.mark.parametrize("inner", [16, 4, 6, 256])
-@pytest.mark.parametrize("layout", ["contiguous", "zigzag"])
+@pytest.mark.parametrize("inner", [16, 4, 6, 256, 80])
+@pytest.mark.parametrize("layout", ["contiguous", "zigzag", "zigzag3", "zigzag4", "striped"])
 def test_layout_gather_bit_exact(inner, layout):
     outer, S, P = 3, 96, 4
     rng = np.random.default_rng([1500, inner])
@@ -224,4 +235,23 @@ def test_layout_gather_bit_exact(inner, layout):
     torch.cuda.synchronize()
     expect = x[:, oracle.natural_positions(S, P, layout)]
     assert np.array_equal(dst.cpu().numpy(), expect)
+    assert np.array_equal(back.cpu().numpy(), x)
+
+
+@pytest.mark.parametrize("inner", [2048, 80, 65552])
+def test_layout_gather_striped_rows(inner):
+    """Striped row copy: rows of 2 KiB (32 rows a work-group), of 80 bytes
+    (5 units, most lanes idle) and of 64 KiB + 16 bytes (4 rows a
+    work-group, a ragged last work-group); S = 1000 over P = 8."""
+    outer, P = 2, 8
+    S = 1000 if inner <= 2048 else 40
+    rng = np.random.default_rng([1502, inner])
+    x = rng.integers(0, 256, size=(outer, S, inner), dtype=np.uint8)
+    src = torch.from_numpy(x).cuda()
+    dst = torch.empty_like(src)
+    back = torch.empty_like(src)
+    ra.ra_layout_gather(src, dst, S, P, "striped", inverse=False)
+    ra.ra_layout_gather(dst, back, S, P, "striped", inverse=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(dst.cpu().numpy(), x[:, oracle.natural_positions(S, P, "striped")])
     assert np.array_equal(back.cpu().numpy(), x)
