@@ -5,7 +5,7 @@ One step runs every stage of the path once, on synthetic inputs already
 resident in HBM:
   1. layout: natural -> zig-zag sharded order of Q, K, V (ra_layout_gather)
      for the 128k-token GQA workload (B1 Hq32 Hkv8 d128 S131072, P8);
-  2. prefill: rank 0's share of ring attention on that workload (ra_fwd_rank:
+  2. prefill: rank 0's share of ring attention on that workload (ra_fwd_rank_ws:
      16384 local queries x 32 heads against all 131072 keys, visited in ring
      order, causal, zig-zag);
   3. decode: KV-sharded decode (B8, 1 query, Hq64 Hkv8 d128, 1,048,576 keys
@@ -20,8 +20,10 @@ the ``decode`` object.  ``cpu_baseline`` times the fp64 CPU oracle on a sample
 of the same prefill workload.
 
 --layout runs the same prefill shape under another split (contiguous,
-striped, zigzag<k>); --all-ranks adds the time of every rank's share, whose
-maximum is the length of one ring step when the ranks run side by side.
+striped, zigzag<k>); --prefill-cfg picks the 32k or 8k-token workload
+instead; --all-ranks adds the time of every rank's share, whose maximum is
+the length of one ring pass when the ranks run side by side, and of all
+ranks in one launch (ra_fwd_all).
 """
 from __future__ import annotations
 
@@ -43,6 +45,7 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 PREFILL_SOURCES = ["fwd_bf16.hip", "ra_device.h", "ra_internal.h"]
 DECODE_SOURCES = ["decode.hip", "ra_device.h", "ra_internal.h"]
+LAYOUT_SOURCES = ["layout.hip", "ra_device.h", "ra_internal.h"]
 
 
 def log(msg: str) -> None:
@@ -57,9 +60,10 @@ def source_hash(files) -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel: str, files):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or
-    None when the kernel source changed since the counters were taken."""
+def measured_traffic(kernel: str, files, key: str = "bytes_per_launch"):
+    """HBM bytes per launch (or per step) from the committed rocprofv3
+    counter summary, or None when the kernel source changed since the
+    counters were taken."""
     try:
         data = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
@@ -67,7 +71,7 @@ def measured_traffic(kernel: str, files):
     rec = data.get(kernel)
     if not rec or rec.get("source_hash") != source_hash(files):
         return None
-    return rec.get("bytes_per_launch")
+    return rec.get(key)
 
 
 def cpu_baseline(w, rank: int, n_rows: int):
@@ -106,6 +110,9 @@ def main() -> int:
     ap.add_argument("--decode-parts", type=int, default=64)
     ap.add_argument("--cpu-rows", type=int, default=128)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefill-cfg", type=int, choices=[2, 3, 4], default=4,
+                    help="prefill workload: 4 = 128k-token GQA (default, the headline), 3 = 32k "
+                         "zig-zag MHA, 2 = 8k contiguous MHA")
     ap.add_argument("--all-ranks", action="store_true",
                     help="also time every rank's share of the prefill (the ring step lasts as "
                          "long as the slowest rank)")
@@ -151,9 +158,9 @@ def main() -> int:
         print(json.dumps({"workload": "copy", "bytes_read": nbytes, "bytes_written": nbytes,
                           "ms": ms, "GB/s": 2 * nbytes / (ms * 1e-3) / 1e9}), flush=True)
         return 0
-    wp, wd = WORKLOADS[4], WORKLOADS[5]
-    own_layout = args.layout is None or args.layout == wp.layout
-    if not own_layout:
+    wp, wd = WORKLOADS[args.prefill_cfg], WORKLOADS[5]
+    own_layout = (args.layout is None or args.layout == wp.layout) and args.prefill_cfg == 4
+    if args.layout is not None:
         wp = dataclasses.replace(wp, layout=args.layout)
 
     launches = []  # (stage, fn)
@@ -168,13 +175,19 @@ def main() -> int:
         Q_r = Qs[:, r * n:(r + 1) * n]
         O_r = torch.empty(Q_r.shape, dtype=torch.float32, device=dev)  # fp32 accumulator output
         L_r = torch.empty(wp.B, wp.Hq, n, dtype=torch.float32, device=dev)
+        # workspace for the automatic key-range splits (none for the 128k
+        # workload, whose rank share already has 2048 query tiles)
+        ws_r_bytes = ra.ra_fwd_workspace_bytes(wp.B, wp.Hq, wp.Hkv, wp.S, wp.d, wp.P, False,
+                                               wp.causal, wp.layout, ra.DTYPE_BF16, 0)
+        ws_r = torch.empty(max(ws_r_bytes, 1), dtype=torch.uint8, device=dev)
+        splits_r = ws_r_bytes // (wp.B * n * wp.Hq * (wp.d + 1) * 4) if ws_r_bytes else 1
 
         def layout():
             for a, b in ((Qn, Qs), (Kn, Ks), (Vn, Vs)):
                 ra.ra_layout_gather(a, b, wp.S, wp.P, wp.layout, inverse=False)
 
         def prefill():
-            ra.ra_fwd_rank(Q_r, Ks, Vs, O_r, L_r, wp.P, r, True, wp.layout)
+            ra.ra_fwd_rank_ws(Q_r, Ks, Vs, O_r, L_r, wp.P, r, wp.causal, wp.layout, 0, ws_r)
 
         launches += [("layout", layout), ("prefill", prefill)]
     if do_dec:
@@ -219,8 +232,12 @@ def main() -> int:
         step(ev[k])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = {name: sum(ev[k][i][0].elapsed_time(ev[k][i][1]) for k in range(args.steps)) / args.steps
-          for i, (name, _) in enumerate(launches)}
+    per_step = {name: sorted(ev[k][i][0].elapsed_time(ev[k][i][1]) for k in range(args.steps))
+                for i, (name, _) in enumerate(launches)}
+    ms = {name: sum(v) / len(v) for name, v in per_step.items()}
+    med = {name: v[len(v) // 2] if len(v) % 2 else 0.5 * (v[len(v) // 2 - 1] + v[len(v) // 2])
+           for name, v in per_step.items()}
+    mn = {name: v[0] for name, v in per_step.items()}
     log("stage ms: " + ", ".join(f"{k}={v:.3f}" for k, v in ms.items()))
 
     out = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -238,13 +255,16 @@ def main() -> int:
                            "traffic": (measured_traffic("prefill", PREFILL_SOURCES)
                                        if own_layout else None),
                            "kernel": "fwd_bf16_kernel<128>", "flops_per_launch": flops,
-                           "ms_per_launch": ms["prefill"]}
+                           "ms_per_launch": ms["prefill"], "ms_median": med["prefill"],
+                           "ms_min": mn["prefill"], "kv_splits": splits_r}
         out["layout"] = {"value": lay_bytes / (ms["layout"] * 1e-3) / 1e9, "unit": "GB/s",
                          "ms": ms["layout"], "bytes": lay_bytes,
+                         "traffic": (measured_traffic("layout", LAYOUT_SOURCES, "bytes_per_step")
+                                     if own_layout else None),
                          "frac_hbm": lay_bytes / (ms["layout"] * 1e-3) / 1e9 / PEAK_HBM_GBS}
         cfg.update({"workload": f"{wp.name} rank-{args.rank} share", "global_batch": wp.B,
                     "seq_len": wp.S, "heads_q": wp.Hq, "heads_kv": wp.Hkv, "head_dim": wp.d,
-                    "ranks": wp.P, "layout": wp.layout, "causal": True})
+                    "ranks": wp.P, "layout": wp.layout, "causal": wp.causal})
     if do_dec:
         nb = decode_bytes(wd, args.decode_parts)
         gbs = nb["attn_partial"] / (ms["decode"] * 1e-3) / 1e9
@@ -256,7 +276,8 @@ def main() -> int:
                                       "traffic": measured_traffic("decode", DECODE_SOURCES),
                                       "kernel": "decode_bf16_kernel<128>",
                                       "bytes_per_launch": nb["attn_partial"],
-                                      "ms_per_launch": ms["decode"]},
+                                      "ms_per_launch": ms["decode"], "ms_median": med["decode"],
+                                      "ms_min": mn["decode"]},
                          "merge_ms": ms["merge"], "parts": args.decode_parts}
         cfg["decode_workload"] = wd.name
         if not do_pre:
@@ -270,15 +291,34 @@ def main() -> int:
         for rr in range(wp.P):
             Qrr = Qs[:, rr * n:(rr + 1) * n]
             for _ in range(args.warmup):
-                ra.ra_fwd_rank(Qrr, Ks, Vs, O_r, L_r, wp.P, rr, True, wp.layout)
+                ra.ra_fwd_rank_ws(Qrr, Ks, Vs, O_r, L_r, wp.P, rr, wp.causal, wp.layout, 0, ws_r)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
             for _ in range(args.steps):
-                ra.ra_fwd_rank(Qrr, Ks, Vs, O_r, L_r, wp.P, rr, True, wp.layout)
+                ra.ra_fwd_rank_ws(Qrr, Ks, Vs, O_r, L_r, wp.P, rr, wp.causal, wp.layout, 0, ws_r)
             e1.record()
             torch.cuda.synchronize()
             per.append(e0.elapsed_time(e1) / args.steps)
         total = prefill_flops(wp)
+        # all ranks in one launch: the whole problem on this one GPU
+        O_all = torch.empty(wp.B, wp.S, wp.Hq, wp.d, dtype=torch.float32, device=dev)
+        L_all = torch.empty(wp.B, wp.Hq, wp.S, dtype=torch.float32, device=dev)
+        ws_a_bytes = ra.ra_fwd_workspace_bytes(wp.B, wp.Hq, wp.Hkv, wp.S, wp.d, wp.P, True,
+                                               wp.causal, wp.layout, ra.DTYPE_BF16, 0)
+        ws_a = torch.empty(max(ws_a_bytes, 1), dtype=torch.uint8, device=dev)
+        for _ in range(args.warmup):
+            ra.ra_fwd_all_ws(Qs, Ks, Vs, O_all, L_all, wp.P, wp.causal, wp.layout, 0, ws_a)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            ra.ra_fwd_all_ws(Qs, Ks, Vs, O_all, L_all, wp.P, wp.causal, wp.layout, 0, ws_a)
+        e1.record()
+        torch.cuda.synchronize()
+        all_ms = e0.elapsed_time(e1) / args.steps
+        splits_a = ws_a_bytes // (wp.B * wp.S * wp.Hq * (wp.d + 1) * 4) if ws_a_bytes else 1
+        del O_all, L_all, ws_a
+        out["fwd_all"] = {"ms": all_ms, "tflops": total / (all_ms * 1e-3) / 1e12,
+                          "kv_splits": splits_a}
         out["ranks"] = {"ms": [round(x, 4) for x in per], "ring_step_ms": max(per),
                         "max_over_min": max(per) / min(per),
                         "gflop": [round(prefill_flops(wp, rr) / 1e9, 1) for rr in range(wp.P)],

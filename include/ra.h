@@ -128,6 +128,49 @@ int ra_fwd_all(const void* Q, const void* K, const void* V, void* O, float* LSE,
                int causal, int layout, int dtype, int o_dtype, void* stream);
 
 /*
+ * ra_fwd_rank_ws, ra_fwd_all_ws -- ra_fwd_rank / ra_fwd_all with a caller
+ * workspace that lets the library split each query tile's walk over the key
+ * tiles (the ring order above) into kv_splits contiguous ranges, run them on
+ * separate work-groups, and combine the (O, lse) partials of the ranges with
+ * the fold of [L8] section 3 (the ra_merge_partials formula).  This keeps the
+ * GPU busy when a launch has few query tiles (a short rank share) or when
+ * one causal tile does much more work than the rest.
+ *   kv_splits  0: automatic (about two work-groups per compute unit, at most
+ *              8 ranges, fewer if the workspace is smaller); 1..RA_MAX_KV_SPLITS:
+ *              exactly that many ranges (a range may be empty).
+ *   workspace  device memory of workspace_bytes, 16-byte aligned, owned by
+ *              the caller, not aliasing any tensor argument; its contents on
+ *              entry do not matter and are garbage on return.  NULL or too
+ *              small: automatic mode uses fewer splits (1 needs none); an
+ *              explicit kv_splits fails with RA_ERR_INVALID_ARG.
+ * All other arguments and requirements are those of ra_fwd_rank / ra_fwd_all.
+ * With one split the result is bit-identical to ra_fwd_rank / ra_fwd_all; for
+ * a given kv_splits the rows of ra_fwd_rank_ws equal those of ra_fwd_all_ws
+ * bit for bit.  Other split counts agree within rounding.
+ */
+#define RA_MAX_KV_SPLITS 64
+
+int ra_fwd_rank_ws(const void* Q_r, const void* K, const void* V, void* O_r, float* LSE_r,
+                   int B, int Hq, int Hkv, int64_t S, int d, int P, int rank,
+                   int causal, int layout, int dtype, int o_dtype,
+                   int kv_splits, void* workspace, int64_t workspace_bytes, void* stream);
+
+int ra_fwd_all_ws(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                  int B, int Hq, int Hkv, int64_t S, int d, int P,
+                  int causal, int layout, int dtype, int o_dtype,
+                  int kv_splits, void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * ra_fwd_workspace_bytes -- workspace that ra_fwd_rank_ws (all_ranks = 0) or
+ * ra_fwd_all_ws (all_ranks = 1) needs for kv_splits ranges (0: the automatic
+ * choice): kv_splits * rows * (d + 1) * 4 bytes with rows = B * Hq * (S/P or S),
+ * 0 for one range.  Returns a negative ra_status for invalid shapes.  No HIP
+ * call is made.
+ */
+int64_t ra_fwd_workspace_bytes(int B, int Hq, int Hkv, int64_t S, int d, int P, int all_ranks,
+                               int causal, int layout, int dtype, int kv_splits);
+
+/*
  * ra_merge_partials -- combine (O, lse) partials that were computed over
  * disjoint key sets of the same query rows ([L8] section 3 applied to whole
  * shards; [HX] phase 1):

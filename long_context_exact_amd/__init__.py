@@ -27,7 +27,8 @@ def layout_zigzag_k(k: int) -> int:
     return 0x100 | int(k)
 DTYPE_F32, DTYPE_BF16 = 0, 1
 
-EXPORTS = ("ra_fwd_rank", "ra_fwd_all", "ra_merge_partials", "ra_attn_partial",
+EXPORTS = ("ra_fwd_rank", "ra_fwd_all", "ra_fwd_rank_ws", "ra_fwd_all_ws", "ra_fwd_workspace_bytes",
+           "ra_merge_partials", "ra_attn_partial",
            "ra_layout_gather", "ra_last_error", "ra_version")
 
 _lib = None
@@ -52,11 +53,17 @@ def lib() -> ctypes.CDLL:
                                   i32, i32, vp]
         L.ra_fwd_all.argtypes = [vp, vp, vp, vp, fp, i32, i32, i32, i64, i32, i32, i32, i32, i32, i32,
                                  vp]
+        L.ra_fwd_rank_ws.argtypes = [vp, vp, vp, vp, fp, i32, i32, i32, i64, i32, i32, i32, i32,
+                                     i32, i32, i32, i32, vp, i64, vp]
+        L.ra_fwd_all_ws.argtypes = [vp, vp, vp, vp, fp, i32, i32, i32, i64, i32, i32, i32, i32,
+                                    i32, i32, i32, vp, i64, vp]
+        L.ra_fwd_workspace_bytes.argtypes = [i32, i32, i32, i64, i32, i32, i32, i32, i32, i32, i32]
+        L.ra_fwd_workspace_bytes.restype = ctypes.c_int64
         L.ra_merge_partials.argtypes = [fp, fp, vp, fp, i32, i64, i32, i32, vp]
         L.ra_attn_partial.argtypes = [vp, vp, vp, fp, fp, i32, i32, i32, i64, i64, i32, i32, i32, vp]
         L.ra_layout_gather.argtypes = [vp, vp, i64, i64, i64, i32, i32, i32, vp]
-        for f in ("ra_fwd_rank", "ra_fwd_all", "ra_merge_partials", "ra_attn_partial",
-                  "ra_layout_gather"):
+        for f in ("ra_fwd_rank", "ra_fwd_all", "ra_fwd_rank_ws", "ra_fwd_all_ws",
+                  "ra_merge_partials", "ra_attn_partial", "ra_layout_gather"):
             getattr(L, f).restype = ctypes.c_int
         L.ra_last_error.restype = ctypes.c_char_p
         L.ra_version.restype = ctypes.c_char_p
@@ -147,6 +154,62 @@ def ra_fwd_all(Q, K, V, O, LSE, P: int, causal: bool, layout, stream=None):
     _check(lib().ra_fwd_all(_dev(Q, "Q"), _dev(K, "K"), _dev(V, "V"), _dev(O, "O"),
                             _dev(LSE, "LSE"), B, Hq, Hkv, S, d, P, int(bool(causal)),
                             _layout(layout), dt, _dtype_code(O), _stream(stream)))
+
+
+def _ws(workspace):
+    if workspace is None:
+        return None, 0
+    return _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
+
+
+def ra_fwd_workspace_bytes(B: int, Hq: int, Hkv: int, S: int, d: int, P: int, all_ranks: bool,
+                           causal: bool, layout, dtype: int, kv_splits: int = 0) -> int:
+    """Workspace bytes ra_fwd_rank_ws (all_ranks False) or ra_fwd_all_ws
+    (True) needs for kv_splits key ranges (0: the automatic choice)."""
+    n = lib().ra_fwd_workspace_bytes(B, Hq, Hkv, S, d, P, int(bool(all_ranks)), int(bool(causal)),
+                                     _layout(layout), int(dtype), int(kv_splits))
+    if n < 0:
+        raise RaError(int(n), last_error())
+    return int(n)
+
+
+def ra_fwd_rank_ws(Q_r, K, V, O_r, LSE_r, P: int, rank: int, causal: bool, layout,
+                   kv_splits: int = 0, workspace=None, stream=None):
+    """ra_fwd_rank with key-range splits merged through ``workspace`` (a
+    device tensor of at least ra_fwd_workspace_bytes bytes, or None)."""
+    B, S, Hkv, d = K.shape
+    Hq = Q_r.shape[2]
+    if tuple(Q_r.shape) != (B, S // P, Hq, d) or O_r.shape != Q_r.shape or V.shape != K.shape:
+        raise ValueError("shape mismatch")
+    if tuple(LSE_r.shape) != (B, Hq, S // P) or LSE_r.dtype != _torch().float32:
+        raise ValueError("LSE_r must be float32 [B, Hq, S/P]")
+    dt = _dtype_code(Q_r)
+    if not (K.dtype == V.dtype == Q_r.dtype):
+        raise TypeError("Q, K, V must share a dtype")
+    wp, wb = _ws(workspace)
+    _check(lib().ra_fwd_rank_ws(_dev(Q_r, "Q_r"), _dev(K, "K"), _dev(V, "V"), _dev(O_r, "O_r"),
+                                _dev(LSE_r, "LSE_r"), B, Hq, Hkv, S, d, P, rank, int(bool(causal)),
+                                _layout(layout), dt, _dtype_code(O_r), int(kv_splits), wp, wb,
+                                _stream(stream)))
+
+
+def ra_fwd_all_ws(Q, K, V, O, LSE, P: int, causal: bool, layout, kv_splits: int = 0,
+                  workspace=None, stream=None):
+    """ra_fwd_all with key-range splits merged through ``workspace``."""
+    B, S, Hkv, d = K.shape
+    Hq = Q.shape[2]
+    if tuple(Q.shape) != (B, S, Hq, d) or O.shape != Q.shape or V.shape != K.shape:
+        raise ValueError("shape mismatch")
+    if tuple(LSE.shape) != (B, Hq, S) or LSE.dtype != _torch().float32:
+        raise ValueError("LSE must be float32 [B, Hq, S]")
+    dt = _dtype_code(Q)
+    if not (K.dtype == V.dtype == Q.dtype):
+        raise TypeError("Q, K, V must share a dtype")
+    wp, wb = _ws(workspace)
+    _check(lib().ra_fwd_all_ws(_dev(Q, "Q"), _dev(K, "K"), _dev(V, "V"), _dev(O, "O"),
+                               _dev(LSE, "LSE"), B, Hq, Hkv, S, d, P, int(bool(causal)),
+                               _layout(layout), dt, _dtype_code(O), int(kv_splits), wp, wb,
+                               _stream(stream)))
 
 
 def ra_merge_partials(O_parts, lse_parts, O, lse=None, stream=None):

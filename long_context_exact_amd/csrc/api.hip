@@ -115,6 +115,9 @@ ra::FwdParams plan_fwd(const void* Q, const void* K, const void* V, void* O, flo
     p.tiles_per_chunk = (int)((p.c + bm - 1) / bm);
     const int pairs = B * Hkv;
     p.xcd_pairs = (pairs % 8 == 0) ? pairs / 8 : 0;
+    p.kv_splits = 1;
+    p.o_split_stride = 0;
+    p.l_split_stride = 0;
     p.scale = (float)(1.0 / sqrt((double)d));
     p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d));
     return p;
@@ -122,11 +125,88 @@ ra::FwdParams plan_fwd(const void* Q, const void* K, const void* V, void* O, flo
 
 int launch_fwd(const ra::FwdParams& p, int d, int dtype, void* stream) {
     const int64_t tiles = (int64_t)p.n_ranks * p.chunks_per_rank * p.tiles_per_chunk;
-    const int64_t grid = tiles * p.B * p.Hq;
+    const int64_t grid = tiles * p.B * p.Hq * p.kv_splits;
     if (grid > 0x7fffffffLL) return fail(RA_ERR_UNSUPPORTED, "grid of %lld work-groups", (long long)grid);
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = dtype == RA_DTYPE_BF16 ? ra::launch_fwd_bf16(p, d, s) : ra::launch_fwd_f32(p, d, s);
     return hip_status(e, "attention kernel launch");
+}
+
+// ---- key-range splits -------------------------------------------------------
+//
+// A launch with fewer query tiles than a few per compute unit leaves CUs idle,
+// and under the causal mask its heaviest tile alone sets the time.  Splitting
+// every tile's visiting order of key tiles into contiguous ranges, one
+// work-group each, and merging the (O, lse) partials with the merge kernel
+// (the section 3 fold over the ranges) evens this out.
+// Measured on the 8k and 32k-token causal workloads: about two work-groups
+// per CU is best; beyond that the fp32 partials cost more traffic than the
+// balance gains (8 ranges beat 16 on a 32-tile rank share).
+constexpr int kComputeUnits = 256;  // MI355X
+constexpr int kAutoMaxSplits = 8;
+
+int64_t fwd_units(const ra::FwdParams& p) {
+    return (int64_t)p.n_ranks * p.chunks_per_rank * p.tiles_per_chunk * p.B * p.Hq;
+}
+
+// splits the automatic choice asks for: about two work-groups per CU
+int auto_splits(const ra::FwdParams& p) {
+    const int64_t units = fwd_units(p);
+    if (units <= 0 || units >= 4 * kComputeUnits) return 1;
+    const int64_t s = (2 * kComputeUnits + units - 1) / units;
+    return (int)(s < kAutoMaxSplits ? s : kAutoMaxSplits);
+}
+
+// workspace for `splits` partials: fp32 O [splits, rows, d] then LSE [splits, rows]
+int64_t split_bytes(const ra::FwdParams& p, int d, int splits) {
+    if (splits <= 1) return 0;
+    const int64_t rows = (int64_t)p.B * p.q_rows * p.Hq;
+    return (int64_t)splits * rows * (d + 1) * (int64_t)sizeof(float);
+}
+
+int fwd_split(ra::FwdParams p, int d, int dtype, int o_dtype, int kv_splits, void* ws,
+              int64_t ws_bytes, void* stream) {
+    if (kv_splits < 0 || kv_splits > RA_MAX_KV_SPLITS)
+        return fail(RA_ERR_INVALID_ARG, "kv_splits=%d outside [0, %d]", kv_splits, RA_MAX_KV_SPLITS);
+    if (ws_bytes < 0) return fail(RA_ERR_INVALID_ARG, "negative workspace size");
+    if (ws == nullptr) ws_bytes = 0;
+    int splits = kv_splits;
+    if (splits == 0) {
+        splits = auto_splits(p);
+        while (splits > 1 && split_bytes(p, d, splits) > ws_bytes) --splits;
+    } else if (split_bytes(p, d, splits) > ws_bytes) {
+        return fail(RA_ERR_INVALID_ARG, "workspace of %lld bytes, %d splits need %lld",
+                    (long long)ws_bytes, splits, (long long)split_bytes(p, d, splits));
+    }
+    if (splits == 1) return launch_fwd(p, d, dtype, stream);
+    if ((uintptr_t)ws % 16 != 0) return fail(RA_ERR_INVALID_ARG, "workspace not 16-byte aligned");
+    const int64_t rows = (int64_t)p.B * p.q_rows * p.Hq;
+    if ((rows + 3) / 4 > 0x7fffffffLL) return fail(RA_ERR_UNSUPPORTED, "too many rows");
+    float* o_parts = (float*)ws;
+    float* l_parts = o_parts + (int64_t)splits * rows * d;
+    void* O = p.O;
+    float* LSE = p.LSE;
+    p.O = o_parts;
+    p.LSE = l_parts;
+    p.o_f32 = 1;
+    p.kv_splits = splits;
+    p.o_split_stride = rows * d;
+    p.l_split_stride = rows;
+    p.xcd_pairs = 0;  // keep the splits of one tile adjacent in dispatch order
+    const int rc = launch_fwd(p, d, dtype, stream);
+    if (rc != RA_OK) return rc;
+    ra::MergeParams m;
+    m.O_parts = o_parts;
+    m.lse_parts = l_parts;
+    m.O = O;
+    m.lse = LSE;
+    m.rows = rows;
+    m.n_parts = splits;
+    m.out_bf16 = o_dtype == RA_DTYPE_BF16;
+    m.lse_bhq = 1;
+    m.q_rows = p.q_rows;
+    m.Hq = p.Hq;
+    return hip_status(ra::launch_merge(m, d, (hipStream_t)stream), "merge kernel launch");
 }
 
 }  // namespace
@@ -154,6 +234,44 @@ int ra_fwd_all(const void* Q, const void* K, const void* V, void* O, float* LSE,
     return launch_fwd(p, d, dtype, stream);
 }
 
+int ra_fwd_rank_ws(const void* Q_r, const void* K, const void* V, void* O_r, float* LSE_r, int B,
+                   int Hq, int Hkv, int64_t S, int d, int P, int rank, int causal, int layout,
+                   int dtype, int o_dtype, int kv_splits, void* workspace, int64_t workspace_bytes,
+                   void* stream) {
+    int rc = check_fwd(Q_r, K, V, O_r, LSE_r, B, Hq, Hkv, S, d, P, causal, layout, dtype, o_dtype);
+    if (rc != RA_OK) return rc;
+    if (rank < 0 || rank >= P) return fail(RA_ERR_INVALID_ARG, "rank %d outside [0, %d)", rank, P);
+    ra::FwdParams p = plan_fwd(Q_r, K, V, O_r, LSE_r, B, Hq, Hkv, S, d, P, causal, layout, dtype,
+                               o_dtype, rank, 1, 1);
+    return fwd_split(p, d, dtype, o_dtype, kv_splits, workspace, workspace_bytes, stream);
+}
+
+int ra_fwd_all_ws(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int Hq,
+                  int Hkv, int64_t S, int d, int P, int causal, int layout, int dtype, int o_dtype,
+                  int kv_splits, void* workspace, int64_t workspace_bytes, void* stream) {
+    int rc = check_fwd(Q, K, V, O, LSE, B, Hq, Hkv, S, d, P, causal, layout, dtype, o_dtype);
+    if (rc != RA_OK) return rc;
+    ra::FwdParams p = plan_fwd(Q, K, V, O, LSE, B, Hq, Hkv, S, d, P, causal, layout, dtype, o_dtype,
+                               0, P, 0);
+    return fwd_split(p, d, dtype, o_dtype, kv_splits, workspace, workspace_bytes, stream);
+}
+
+int64_t ra_fwd_workspace_bytes(int B, int Hq, int Hkv, int64_t S, int d, int P, int all_ranks,
+                               int causal, int layout, int dtype, int kv_splits) {
+    static const char kDummy = 0;
+    const void* x = &kDummy;  // shape checks only: no tensor is touched
+    int rc = check_fwd(x, x, x, (void*)x, (float*)x, B, Hq, Hkv, S, d, P, causal, layout, dtype,
+                       dtype);
+    if (rc != RA_OK) return rc;
+    if (all_ranks != 0 && all_ranks != 1) return fail(RA_ERR_INVALID_ARG, "all_ranks must be 0 or 1");
+    if (kv_splits < 0 || kv_splits > RA_MAX_KV_SPLITS)
+        return fail(RA_ERR_INVALID_ARG, "kv_splits=%d outside [0, %d]", kv_splits, RA_MAX_KV_SPLITS);
+    ra::FwdParams p = plan_fwd(x, x, x, (void*)x, (float*)x, B, Hq, Hkv, S, d, P, causal, layout,
+                               dtype, dtype, 0, all_ranks ? P : 1, all_ranks ? 0 : 1);
+    ok();
+    return split_bytes(p, d, kv_splits == 0 ? auto_splits(p) : kv_splits);
+}
+
 int ra_merge_partials(const float* O_parts, const float* lse_parts, void* O, float* lse,
                       int n_parts, int64_t rows, int d, int out_dtype, void* stream) {
     if (!O_parts || !lse_parts || !O) return fail(RA_ERR_INVALID_ARG, "null tensor pointer");
@@ -172,6 +290,9 @@ int ra_merge_partials(const float* O_parts, const float* lse_parts, void* O, flo
     p.rows = rows;
     p.n_parts = n_parts;
     p.out_bf16 = out_dtype == RA_DTYPE_BF16;
+    p.lse_bhq = 0;
+    p.q_rows = 0;
+    p.Hq = 1;
     return hip_status(ra::launch_merge(p, d, (hipStream_t)stream), "merge kernel launch");
 }
 

@@ -232,6 +232,18 @@ __device__ __forceinline__ void cur_next(const FwdParams& p, int rank, int qmax,
     }
 }
 
+// skip k tiles (whole segments at a time)
+__device__ __forceinline__ void cur_advance(const FwdParams& p, int rank, int qmax, KvCur& c, int k) {
+    while (k > c.tl) {
+        k -= c.tl + 1;
+        cur_skip(p, rank, qmax, c);
+    }
+    c.tl -= k;
+    c.krow += k * BN;
+    c.kpos += k * BN;
+    c.cleft -= k * BN;
+}
+
 __device__ __forceinline__ int cur_count(const FwdParams& p, int rank, int qmax) {
     KvCur c;
     int n = 0;
@@ -290,7 +302,9 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdParams p) {
     __shared__ __attribute__((aligned(1024))) uint16_t ldsK[NBUF][T::ELEMS];
     __shared__ __attribute__((aligned(1024))) uint16_t ldsV[NBUF][T::ELEMS];
 
-    const QTile qt = decode_qtile<BM>(p, blockIdx.x);
+    // work-group -> (query tile, key range): the splits of one tile are adjacent
+    const unsigned split = blockIdx.x % (unsigned)p.kv_splits;
+    const QTile qt = decode_qtile<BM>(p, blockIdx.x / (unsigned)p.kv_splits);
     const int t = threadIdx.x;
     const int lane = t & 63;
     const int w = __builtin_amdgcn_readfirstlane(t >> 6);  // wave index, uniform in the wave
@@ -333,11 +347,15 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdParams p) {
 
     // ---- prologue: tiles 0 and 1 on their way into buffers 0 and 1; the V
     // buffer "before" tile 0 zeroed (the first PV product multiplies P = 0)
-    const int n = cur_count(p, qt.rank, qmax);
+    // this work-group's key range: tiles [i0, i1) of the tile's visiting order
+    const int n_all = cur_count(p, qt.rank, qmax);
+    const int i0 = (int)(((int64_t)n_all * split) / p.kv_splits);
+    const int n = (int)(((int64_t)n_all * (split + 1)) / p.kv_splits) - i0;
     KvCur it_c, it_l;  // tile i of the loop; last tile whose loads were issued
     int issued = 0;    // tiles whose loads were issued
     if (n > 0) {
         cur_first(p, qt.rank, qmax, it_c);
+        cur_advance(p, qt.rank, qmax, it_c, i0);
         it_l = it_c;
         T::load(Kg + it_l.krow * row_stride, Vg + it_l.krow * row_stride, offs, min(it_l.cleft, BN),
                 row_bytes, ldsK[0], ldsV[0], w, lane);
@@ -538,7 +556,9 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdParams p) {
     const float lr_tot = halves_sum(lr_run);
     const float inv = lr_tot > 0.f ? 1.f / lr_tot : 0.f;
     if (qi < qt.rows) {
-        const int64_t obase = ((qt.b * p.q_rows + qt.q_row0 + qi) * p.Hq + qt.qh) * (int64_t)D;
+        // a split writes its partial into its own slice of the partial buffers
+        const int64_t obase = ((qt.b * p.q_rows + qt.q_row0 + qi) * p.Hq + qt.qh) * (int64_t)D +
+                              (int64_t)split * p.o_split_stride;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -559,7 +579,8 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdParams p) {
             }
         if (h == 0) {
             const float lse = l_tot > 0.f ? (m_ref + __log2f(l_tot)) * kLn2 : kNegInf;
-            p.LSE[((int64_t)qt.b * p.Hq + qt.qh) * p.q_rows + qt.q_row0 + qi] = lse;
+            p.LSE[((int64_t)qt.b * p.Hq + qt.qh) * p.q_rows + qt.q_row0 + qi +
+                  (int64_t)split * p.l_split_stride] = lse;
         }
     }
 }
@@ -568,7 +589,7 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdParams p) {
 
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, hipStream_t s) {
     const int64_t tiles = (int64_t)p.n_ranks * p.chunks_per_rank * p.tiles_per_chunk;
-    const int64_t grid = tiles * p.B * p.Hq;
+    const int64_t grid = tiles * p.B * p.Hq * p.kv_splits;
     if (grid <= 0) return hipSuccess;
     if (d == 128)
         hipLaunchKernelGGL(fwd_bf16_kernel<128>, dim3((unsigned)grid), dim3(NT), 0, s, p);

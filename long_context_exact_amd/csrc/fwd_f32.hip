@@ -21,7 +21,8 @@ __global__ __launch_bounds__(NT) void fwd_f32_kernel(FwdParams p) {
     __shared__ float Ks[BN][D];
     __shared__ float Vs[BN][D];
 
-    const QTile qt = decode_qtile<BM>(p, blockIdx.x);
+    const unsigned split = blockIdx.x % (unsigned)p.kv_splits;
+    const QTile qt = decode_qtile<BM>(p, blockIdx.x / (unsigned)p.kv_splits);
     const int t = threadIdx.x;
     const int qi = t >> 2, part = t & 3;
     const bool qvalid = qi < qt.rows;
@@ -41,8 +42,13 @@ __global__ __launch_bounds__(NT) void fwd_f32_kernel(FwdParams p) {
     const float* Kg = (const float*)p.K + ((int64_t)qt.b * p.S * p.Hkv + qt.kvh) * D;
     const float* Vg = (const float*)p.V + ((int64_t)qt.b * p.S * p.Hkv + qt.kvh) * D;
 
+    // this work-group's key range: tiles [i0, i0 + cnt) of the visiting order
+    const int n_all = kv_count(p, qt.rank, qmax, BN);
+    const int i0 = (int)(((int64_t)n_all * split) / p.kv_splits);
+    int cnt = (int)(((int64_t)n_all * (split + 1)) / p.kv_splits) - i0;
     KvIter it;
-    bool have = kv_first(p, qt.rank, qmax, BN, it);
+    bool have = cnt > 0 && kv_first(p, qt.rank, qmax, BN, it);
+    for (int k = 0; have && k < i0; ++k) have = kv_next(p, qt.rank, qmax, BN, it);
     while (have) {
         const int64_t r0 = it.krow + (int64_t)it.tile * BN;
         const int64_t kpos0 = it.kpos + (int64_t)it.tile * BN;
@@ -92,17 +98,19 @@ __global__ __launch_bounds__(NT) void fwd_f32_kernel(FwdParams p) {
             for (int j = 0; j < BN; ++j) acc = __builtin_fmaf(s[j], Vs[j][4 * e + part], acc);
             o[e] = acc;
         }
-        have = kv_next(p, qt.rank, qmax, BN, it);
+        have = --cnt > 0 && kv_next(p, qt.rank, qmax, BN, it);
     }
 
     if (qvalid) {
         const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-        float* Op = (float*)p.O + ((qt.b * p.q_rows + qt.q_row0 + qi) * p.Hq + qt.qh) * (int64_t)D;
+        float* Op = (float*)p.O + ((qt.b * p.q_rows + qt.q_row0 + qi) * p.Hq + qt.qh) * (int64_t)D +
+                    (int64_t)split * p.o_split_stride;
 #pragma unroll
         for (int e = 0; e < DP; ++e) Op[4 * e + part] = o[e] * inv;
         if (part == 0) {
             const float lse = l_run > 0.f ? m_run * kLn2 + __logf(l_run) : kNegInf;
-            p.LSE[((int64_t)qt.b * p.Hq + qt.qh) * p.q_rows + qt.q_row0 + qi] = lse;
+            p.LSE[((int64_t)qt.b * p.Hq + qt.qh) * p.q_rows + qt.q_row0 + qi +
+                  (int64_t)split * p.l_split_stride] = lse;
         }
     }
 }
@@ -111,7 +119,7 @@ __global__ __launch_bounds__(NT) void fwd_f32_kernel(FwdParams p) {
 
 hipError_t launch_fwd_f32(const FwdParams& p, int d, hipStream_t s) {
     const int64_t tiles = (int64_t)p.n_ranks * p.chunks_per_rank * p.tiles_per_chunk;
-    const int64_t grid = tiles * p.B * p.Hq;
+    const int64_t grid = tiles * p.B * p.Hq * p.kv_splits;
     if (grid <= 0) return hipSuccess;
     if (d == 128)
         hipLaunchKernelGGL(fwd_f32_kernel<128>, dim3((unsigned)grid), dim3(NT), 0, s, p);

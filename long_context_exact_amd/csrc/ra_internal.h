@@ -42,6 +42,12 @@ struct FwdParams {
     int tiles_per_chunk;   // ceil(c / BLOCK_M)
     int chunks_per_rank;   // k: 1 contiguous or striped, k >= 2 zig-zag
     int xcd_pairs;     // (b, kv head) pairs per XCD group, 0 = no XCD grouping
+    // Key-range splits: each query tile's visiting order of key tiles is cut
+    // into kv_splits contiguous ranges, one work-group each.  With more than
+    // one split, O and LSE point at fp32 partial buffers and split s writes
+    // its (O, LSE) partial at offsets s * o_split_stride / s * l_split_stride.
+    int kv_splits;
+    int64_t o_split_stride, l_split_stride;
     float scale_log2;  // log2(e) / sqrt(d)
     float scale;       // 1 / sqrt(d)
 };
@@ -68,6 +74,11 @@ struct MergeParams {
     int64_t rows;
     int n_parts;
     int out_bf16;
+    // lse_bhq = 1: rows are (b, q, h) of a [B, q_rows, Hq, d] output whose LSE
+    // is laid out [B, Hq, q_rows] (partials and result alike); 0: lse[row]
+    int lse_bhq;
+    int64_t q_rows;
+    int Hq;
 };
 
 // Launchers (each returns hipSuccess or the launch error).

@@ -120,3 +120,44 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(ra, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(ImportError):
         ra.lib()
+
+
+def test_fwd_ws_rejects_before_the_device():
+    L = ra.lib()
+
+    def call(kv_splits, ws=NULL, ws_bytes=0, rank=0, **kw):
+        a = dict(B=1, Hq=8, Hkv=8, S=8192, d=128, P=8, causal=1, layout=1, dtype=1, o_dtype=0)
+        a.update(kw)
+        return L.ra_fwd_rank_ws(FAKE, FAKE, FAKE, FAKE, FAKE, a["B"], a["Hq"], a["Hkv"], a["S"],
+                                a["d"], a["P"], rank, a["causal"], a["layout"], a["dtype"],
+                                a["o_dtype"], kv_splits, ws, ws_bytes, NULL)
+
+    assert call(-1) == ra.RA_ERR_INVALID_ARG
+    assert call(65) == ra.RA_ERR_INVALID_ARG                     # above RA_MAX_KV_SPLITS
+    assert call(2) == ra.RA_ERR_INVALID_ARG                      # explicit splits, no workspace
+    assert "workspace" in ra.last_error()
+    need = ra.ra_fwd_workspace_bytes(1, 8, 8, 8192, 128, 8, False, True, "zigzag", 1, 2)
+    assert call(2, FAKE, need - 1) == ra.RA_ERR_INVALID_ARG      # one byte short
+    assert call(2, FAKE, -5) == ra.RA_ERR_INVALID_ARG
+    assert call(0, rank=8) == ra.RA_ERR_INVALID_ARG
+    assert call(0, layout=9) == ra.RA_ERR_INVALID_ARG
+    assert L.ra_fwd_all_ws(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 4, 4, 1000, 64, 3, 0, 0, 0, 0, 0, NULL, 0,
+                           NULL) == ra.RA_ERR_UNSUPPORTED
+
+
+def test_fwd_workspace_bytes():
+    # kv_splits * rows * (d + 1) * 4 with rows = B * Hq * (S/P for a rank, S for all ranks)
+    f = ra.ra_fwd_workspace_bytes
+    assert f(2, 4, 2, 640, 128, 4, False, True, "zigzag", 1, 3) == 3 * (2 * 4 * 160) * 129 * 4
+    assert f(2, 4, 2, 640, 128, 4, True, True, "zigzag", 1, 3) == 3 * (2 * 4 * 640) * 129 * 4
+    assert f(1, 8, 8, 8192, 64, 8, False, True, "contiguous", 1, 1) == 0
+    # automatic: the 128k-token GQA rank share has 2048 tiles (no split); the
+    # 8k-token MHA rank share has 32 (8 ranges, the cap)
+    assert f(1, 32, 8, 131072, 128, 8, False, True, "zigzag", 1, 0) == 0
+    assert f(1, 8, 8, 8192, 128, 8, False, True, "contiguous", 1, 0) == 8 * (8 * 1024) * 129 * 4
+    # the 32k-token zig-zag rank share: 256 tiles, 2 ranges
+    assert f(1, 16, 16, 32768, 128, 8, False, True, "zigzag", 1, 0) == 2 * (16 * 4096) * 129 * 4
+    with pytest.raises(ra.RaError):
+        f(1, 8, 8, 8200, 128, 8, False, True, "zigzag", 1, 0)
+    with pytest.raises(ra.RaError):
+        f(1, 8, 8, 8192, 128, 8, False, True, "zigzag", 1, 65)

@@ -255,3 +255,82 @@ def test_layout_gather_striped_rows(inner):
     torch.cuda.synchronize()
     assert np.array_equal(dst.cpu().numpy(), x[:, oracle.natural_positions(S, P, "striped")])
     assert np.array_equal(back.cpu().numpy(), x)
+
+
+SPLIT = [  # B, S, Hq, Hkv, d, P, layout, causal, dtype
+    (1, 2048, 4, 4, 128, 4, "zigzag", True, "bf16"),     # chunks of 256: one query tile each
+    (2, 640, 4, 2, 128, 4, "zigzag", True, "bf16"),      # chunks of 80
+    (1, 1024, 2, 2, 64, 8, "contiguous", True, "bf16"),  # shards of 128
+    (1, 1040, 4, 2, 128, 4, "striped", True, "bf16"),
+    (1, 1200, 2, 1, 128, 5, "zigzag", False, "bf16"),
+    (1, 520, 4, 2, 64, 4, "zigzag", True, "f32"),
+    (1, 384, 2, 2, 128, 3, "zigzag4", True, "f32"),
+]
+
+
+@pytest.mark.parametrize("case", SPLIT, ids=[_id(c) for c in SPLIT])
+def test_prefill_key_range_splits(case):
+    """ra_fwd_rank_ws / ra_fwd_all_ws: every split count agrees with the
+    oracle; one split is bit-identical to the unsplit entry points; the rows
+    of a rank launch equal those of the all-ranks launch for the same count;
+    a bf16 output is the fp32 result rounded; the workspace may hold garbage."""
+    B, S, Hq, Hkv, d, P, layout, causal, dtype = case
+    log(f"splits {_id(case)}")
+    Qn, Kn, Vn = qkv(B, S, S, Hq, Hkv, d, dtype, (1200, S, P))
+    (Qs, Ks, Vs), O1, L1 = _run_prefill(Qn, Kn, Vn, P, layout, causal, dtype)
+    O_ref, lse_ref = oracle.attention(Qn, Kn, Vn, causal)
+    n = S // P
+    code = 1 if dtype == "bf16" else 0
+    for splits in (1, 2, 3, 7, 0):
+        nb = ra.ra_fwd_workspace_bytes(B, Hq, Hkv, S, d, P, True, causal, layout, code, splits)
+        ws = torch.full((max(nb, 16) // 4,), float("nan"), dtype=torch.float32, device="cuda")
+        O = torch.empty_like(O1)
+        L = torch.empty_like(L1)
+        ra.ra_fwd_all_ws(Qs, Ks, Vs, O, L, P, causal, layout, splits, ws)
+        torch.cuda.synchronize()
+        if splits == 1:
+            assert torch.equal(O, O1) and torch.equal(L, L1)
+        e = check(unshard(from_dev(O), S, P, layout, axis=1), O_ref,
+                  unshard(from_dev(L), S, P, layout, axis=2), lse_ref, dtype,
+                  f"{_id(case)} splits={splits}")
+        log(f"  splits={splits} ok {fmt(e)}")
+        if splits == 0:
+            continue
+        for r in (0, P - 1):
+            nbr = ra.ra_fwd_workspace_bytes(B, Hq, Hkv, S, d, P, False, causal, layout, code, splits)
+            wsr = torch.full((max(nbr, 16) // 4,), float("nan"), dtype=torch.float32, device="cuda")
+            Qr = Qs[:, r * n:(r + 1) * n].contiguous()
+            Or = torch.empty(Qr.shape, dtype=O.dtype, device="cuda")
+            Lr = torch.empty(B, Hq, n, dtype=torch.float32, device="cuda")
+            ra.ra_fwd_rank_ws(Qr, Ks, Vs, Or, Lr, P, r, causal, layout, splits, wsr)
+            torch.cuda.synchronize()
+            assert torch.equal(Or, O[:, r * n:(r + 1) * n]), f"rank {r} splits {splits}"
+            assert torch.equal(Lr, L[:, :, r * n:(r + 1) * n])
+        if dtype == "bf16" and splits == 3:
+            Ob = torch.empty(O.shape, dtype=torch.bfloat16, device="cuda")
+            Lb = torch.empty_like(L)
+            ra.ra_fwd_all_ws(Qs, Ks, Vs, Ob, Lb, P, causal, layout, splits, ws)
+            torch.cuda.synchronize()
+            assert torch.equal(Ob.view(torch.int16), O.to(torch.bfloat16).view(torch.int16))
+            assert torch.equal(Lb, L)
+
+
+def test_prefill_auto_splits_fall_back_to_smaller_workspace():
+    # a workspace that holds two ranges only: the automatic choice uses two
+    B, S, Hq, Hkv, d, P = 1, 1024, 2, 2, 64, 8
+    Qn, Kn, Vn = qkv(B, S, S, Hq, Hkv, d, "bf16", (1201,))
+    (Qs, Ks, Vs), _, _ = _run_prefill(Qn, Kn, Vn, P, "contiguous", True, "bf16")
+    O_ref, lse_ref = oracle.attention(Qn, Kn, Vn, True)
+    two = ra.ra_fwd_workspace_bytes(B, Hq, Hkv, S, d, P, True, True, "contiguous", 1, 2)
+    assert ra.ra_fwd_workspace_bytes(B, Hq, Hkv, S, d, P, True, True, "contiguous", 1, 0) > two
+    ws = torch.empty(two, dtype=torch.uint8, device="cuda")
+    outs = []
+    for splits, w in ((0, ws), (2, ws), (0, None)):
+        O = torch.empty(B, S, Hq, d, dtype=torch.float32, device="cuda")
+        L = torch.empty(B, Hq, S, dtype=torch.float32, device="cuda")
+        ra.ra_fwd_all_ws(Qs, Ks, Vs, O, L, P, True, "contiguous", splits, w)
+        torch.cuda.synchronize()
+        outs.append((O, L))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    check(from_dev(outs[2][0]), O_ref, from_dev(outs[2][1]), lse_ref, "bf16", "no workspace")
+    check(from_dev(outs[0][0]), O_ref, from_dev(outs[0][1]), lse_ref, "bf16", "two ranges")
