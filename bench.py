@@ -21,7 +21,9 @@ of the same prefill workload.
 
 --layout runs the same prefill shape under another split (contiguous,
 striped, zigzag<k>); --prefill-cfg picks the 32k or 8k-token workload
-instead; --all-ranks adds the time of every rank's share, whose maximum is
+instead; --ring-steps times the rank share as P separate ring steps with
+the state in HBM (blocks resident, and double-buffered copies on a second
+stream standing in for the peer-to-peer receive); --all-ranks adds the time of every rank's share, whose maximum is
 the length of one ring pass when the ranks run side by side, and of all
 ranks in one launch (ra_fwd_all).
 """
@@ -116,6 +118,9 @@ def main() -> int:
     ap.add_argument("--all-ranks", action="store_true",
                     help="also time every rank's share of the prefill (the ring step lasts as "
                          "long as the slowest rank)")
+    ap.add_argument("--ring-steps", action="store_true",
+                    help="also time the timed rank's share as P ring steps (ra_ring_step) on one "
+                         "stream, and double-buffered with the next block copied on a second stream")
     ap.add_argument("--layout", default=None,
                     help="prefill split: the workload's own (zig-zag, default) or another one "
                          "(contiguous, striped, zigzag<k>) on the same shape")
@@ -323,6 +328,70 @@ def main() -> int:
                         "max_over_min": max(per) / min(per),
                         "gflop": [round(prefill_flops(wp, rr) / 1e9, 1) for rr in range(wp.P)],
                         "tflops_per_gpu_at_ring_step": total / wp.P / (max(per) * 1e-3) / 1e12}
+    if do_pre and args.ring_steps:
+        log(f"timing rank {r} as {wp.P} ring steps")
+        O_s = torch.empty(Q_r.shape, dtype=torch.float32, device=dev)
+        L_s = torch.empty_like(L_r)
+        Q_rc = Q_r.contiguous()
+
+        def block(x, s_):
+            return x[:, s_ * n:(s_ + 1) * n]
+
+        def steps_resident():
+            for t in range(wp.P):
+                s_ = (r - t) % wp.P
+                ra.ra_ring_step(Q_rc, block(Ks, s_), block(Vs, s_), O_s, L_s, wp.S, wp.P, r, t,
+                                wp.causal, wp.layout)
+
+        comp = torch.cuda.current_stream()
+        copy = torch.cuda.Stream()
+        bufK = [torch.empty(block(Ks, 0).shape, dtype=Ks.dtype, device=dev) for _ in range(2)]
+        bufV = [torch.empty_like(bufK[0]) for _ in range(2)]
+        arrived = [torch.cuda.Event() for _ in range(2)]
+        free = [torch.cuda.Event() for _ in range(2)]
+
+        def receive(t):
+            s_ = (r - t) % wp.P
+            with torch.cuda.stream(copy):
+                copy.wait_event(free[t % 2])
+                bufK[t % 2].copy_(block(Ks, s_))
+                bufV[t % 2].copy_(block(Vs, s_))
+                arrived[t % 2].record(copy)
+
+        def steps_double_buffered():
+            for e in free:
+                e.record(comp)
+            receive(0)
+            for t in range(wp.P):
+                if t + 1 < wp.P:
+                    receive(t + 1)
+                comp.wait_event(arrived[t % 2])
+                ra.ra_ring_step(Q_rc, bufK[t % 2], bufV[t % 2], O_s, L_s, wp.S, wp.P, r, t,
+                                wp.causal, wp.layout)
+                free[t % 2].record(comp)
+
+        def time_fn(fn):
+            for _ in range(args.warmup):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(args.steps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / args.steps
+
+        if wp.B == 1:  # a shard of a [1, S, H, d] tensor is a contiguous block
+            t_res = time_fn(steps_resident)
+        else:
+            t_res = None
+        t_db = time_fn(steps_double_buffered)
+        blk_bytes = 2 * bufK[0].numel() * bufK[0].element_size()
+        out["ring_steps"] = {"steps": wp.P, "resident_ms": t_res, "double_buffered_ms": t_db,
+                             "fused_ms": ms["prefill"], "block_bytes_per_step": blk_bytes,
+                             "overhead_vs_fused": t_db / ms["prefill"] - 1.0}
+        del O_s, L_s, bufK, bufV
     if do_pre and not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on {args.cpu_rows} sampled rows")
         out["cpu_baseline"] = cpu_baseline(wp, args.rank, args.cpu_rows)

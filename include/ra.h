@@ -161,6 +161,34 @@ int ra_fwd_all_ws(const void* Q, const void* K, const void* V, void* O, float* L
                   int kv_splits, void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
+ * ra_ring_step -- one step of the ring loop of one rank ([L8] section 2),
+ * for a deployment where K/V blocks arrive one at a time (a P2P receive
+ * buffer) instead of all being resident.
+ *
+ * At step t rank `rank` holds the K/V block of shard s = (rank - t) mod P.
+ * The call attends the rank's queries to that block (causal mask on global
+ * positions, as ra_fwd_rank) and folds the result into the running state
+ * (O_acc, LSE_acc) with the update of [L8] section 3 applied to the whole
+ * block: M = max(lse_old, lse_t), a = e^(lse_old-M), b = e^(lse_t-M),
+ * O = (a O_old + b O_t)/(a+b), LSE = M + ln(a+b).
+ *   Q_r          [B, S/P, Hq, d]   the rank's local queries (dtype)
+ *   K_blk, V_blk [B, S/P, Hkv, d]  shard s's rows in sharded order (dtype)
+ *   O_acc        [B, S/P, Hq, d]   fp32 running output, normalised
+ *   LSE_acc      [B, Hq, S/P]      fp32 running LSE
+ * Step t = 0 initialises the state (its previous contents do not matter);
+ * steps t > 0 fold into it and may come in any order after t = 0.  After
+ * all P steps O_acc and LSE_acc equal ra_fwd_rank's fp32 output within
+ * rounding (the fold reference points differ).  A bf16 copy of O_acc is
+ * ra_merge_partials(O_acc, LSE_acc, O, NULL, 1, rows, d, RA_DTYPE_BF16).
+ * Requirements: those of ra_fwd_rank, 0 <= t < P; the state must not alias
+ * Q_r or the block.  Launches of one rank's steps must be ordered (one
+ * stream, or events): each reads and writes the whole state.
+ */
+int ra_ring_step(const void* Q_r, const void* K_blk, const void* V_blk, float* O_acc,
+                 float* LSE_acc, int B, int Hq, int Hkv, int64_t S, int d, int P, int rank,
+                 int t, int causal, int layout, int dtype, void* stream);
+
+/*
  * ra_fwd_workspace_bytes -- workspace that ra_fwd_rank_ws (all_ranks = 0) or
  * ra_fwd_all_ws (all_ranks = 1) needs for kv_splits ranges (0: the automatic
  * choice): kv_splits * rows * (d + 1) * 4 bytes with rows = B * Hq * (S/P or S),

@@ -28,6 +28,7 @@ def layout_zigzag_k(k: int) -> int:
 DTYPE_F32, DTYPE_BF16 = 0, 1
 
 EXPORTS = ("ra_fwd_rank", "ra_fwd_all", "ra_fwd_rank_ws", "ra_fwd_all_ws", "ra_fwd_workspace_bytes",
+           "ra_ring_step",
            "ra_merge_partials", "ra_attn_partial",
            "ra_layout_gather", "ra_last_error", "ra_version")
 
@@ -58,11 +59,13 @@ def lib() -> ctypes.CDLL:
         L.ra_fwd_all_ws.argtypes = [vp, vp, vp, vp, fp, i32, i32, i32, i64, i32, i32, i32, i32,
                                     i32, i32, i32, vp, i64, vp]
         L.ra_fwd_workspace_bytes.argtypes = [i32, i32, i32, i64, i32, i32, i32, i32, i32, i32, i32]
+        L.ra_ring_step.argtypes = [vp, vp, vp, fp, fp, i32, i32, i32, i64, i32, i32, i32, i32, i32,
+                                   i32, i32, vp]
         L.ra_fwd_workspace_bytes.restype = ctypes.c_int64
         L.ra_merge_partials.argtypes = [fp, fp, vp, fp, i32, i64, i32, i32, vp]
         L.ra_attn_partial.argtypes = [vp, vp, vp, fp, fp, i32, i32, i32, i64, i64, i32, i32, i32, vp]
         L.ra_layout_gather.argtypes = [vp, vp, i64, i64, i64, i32, i32, i32, vp]
-        for f in ("ra_fwd_rank", "ra_fwd_all", "ra_fwd_rank_ws", "ra_fwd_all_ws",
+        for f in ("ra_fwd_rank", "ra_fwd_all", "ra_fwd_rank_ws", "ra_fwd_all_ws", "ra_ring_step",
                   "ra_merge_partials", "ra_attn_partial", "ra_layout_gather"):
             getattr(L, f).restype = ctypes.c_int
         L.ra_last_error.restype = ctypes.c_char_p
@@ -210,6 +213,28 @@ def ra_fwd_all_ws(Q, K, V, O, LSE, P: int, causal: bool, layout, kv_splits: int 
                                _dev(LSE, "LSE"), B, Hq, Hkv, S, d, P, int(bool(causal)),
                                _layout(layout), dt, _dtype_code(O), int(kv_splits), wp, wb,
                                _stream(stream)))
+
+
+def ra_ring_step(Q_r, K_blk, V_blk, O_acc, LSE_acc, S: int, P: int, rank: int, t: int,
+                 causal: bool, layout, stream=None):
+    """One ring step: fold the block of shard (rank - t) mod P (K_blk, V_blk
+    [B, S/P, Hkv, d]) into the running fp32 state O_acc [B, S/P, Hq, d],
+    LSE_acc [B, Hq, S/P] of the rank's queries Q_r [B, S/P, Hq, d]."""
+    B, n, Hkv, d = K_blk.shape
+    Hq = Q_r.shape[2]
+    torch = _torch()
+    if n * P != S or tuple(Q_r.shape) != (B, n, Hq, d) or V_blk.shape != K_blk.shape:
+        raise ValueError("shape mismatch")
+    if O_acc.shape != Q_r.shape or O_acc.dtype != torch.float32:
+        raise ValueError("O_acc must be float32 [B, S/P, Hq, d]")
+    if tuple(LSE_acc.shape) != (B, Hq, n) or LSE_acc.dtype != torch.float32:
+        raise ValueError("LSE_acc must be float32 [B, Hq, S/P]")
+    if not (K_blk.dtype == V_blk.dtype == Q_r.dtype):
+        raise TypeError("Q, K, V must share a dtype")
+    _check(lib().ra_ring_step(_dev(Q_r, "Q_r"), _dev(K_blk, "K_blk"), _dev(V_blk, "V_blk"),
+                              _dev(O_acc, "O_acc"), _dev(LSE_acc, "LSE_acc"), B, Hq, Hkv, S, d, P,
+                              rank, t, int(bool(causal)), _layout(layout), _dtype_code(Q_r),
+                              _stream(stream)))
 
 
 def ra_merge_partials(O_parts, lse_parts, O, lse=None, stream=None):

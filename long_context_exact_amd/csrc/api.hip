@@ -118,6 +118,11 @@ ra::FwdParams plan_fwd(const void* Q, const void* K, const void* V, void* O, flo
     p.kv_splits = 1;
     p.o_split_stride = 0;
     p.l_split_stride = 0;
+    p.step_lo = 0;
+    p.step_hi = P;
+    p.kv_block = 0;
+    p.kv_rows = S;
+    p.fold = 0;
     p.scale = (float)(1.0 / sqrt((double)d));
     p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d));
     return p;
@@ -254,6 +259,24 @@ int ra_fwd_all_ws(const void* Q, const void* K, const void* V, void* O, float* L
     ra::FwdParams p = plan_fwd(Q, K, V, O, LSE, B, Hq, Hkv, S, d, P, causal, layout, dtype, o_dtype,
                                0, P, 0);
     return fwd_split(p, d, dtype, o_dtype, kv_splits, workspace, workspace_bytes, stream);
+}
+
+int ra_ring_step(const void* Q_r, const void* K_blk, const void* V_blk, float* O_acc, float* LSE_acc,
+                 int B, int Hq, int Hkv, int64_t S, int d, int P, int rank, int t, int causal,
+                 int layout, int dtype, void* stream) {
+    int rc = check_fwd(Q_r, K_blk, V_blk, O_acc, LSE_acc, B, Hq, Hkv, S, d, P, causal, layout, dtype,
+                       RA_DTYPE_F32);
+    if (rc != RA_OK) return rc;
+    if (rank < 0 || rank >= P) return fail(RA_ERR_INVALID_ARG, "rank %d outside [0, %d)", rank, P);
+    if (t < 0 || t >= P) return fail(RA_ERR_INVALID_ARG, "step %d outside [0, %d)", t, P);
+    ra::FwdParams p = plan_fwd(Q_r, K_blk, V_blk, O_acc, LSE_acc, B, Hq, Hkv, S, d, P, causal, layout,
+                               dtype, RA_DTYPE_F32, rank, 1, 1);
+    p.step_lo = t;
+    p.step_hi = t + 1;
+    p.kv_block = 1;
+    p.kv_rows = p.n;
+    p.fold = t > 0;
+    return launch_fwd(p, d, dtype, stream);
 }
 
 int64_t ra_fwd_workspace_bytes(int B, int Hq, int Hkv, int64_t S, int d, int P, int all_ranks,

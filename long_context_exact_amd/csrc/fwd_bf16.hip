@@ -196,7 +196,7 @@ __device__ __forceinline__ bool cur_seg(const FwdParams& p, int rank, int qmax, 
     int s = rank - c.t;
     if (s < 0) s += p.P;
     const int cl = (int)p.c;
-    c.krow = s * (int)p.n + c.lc * cl;
+    c.krow = (p.kv_block ? 0 : s * (int)p.n) + c.lc * cl;
     c.kpos = p.striped ? (int)(s > rank) : global_chunk(p.P, p.chunks_per_rank, s, c.lc) * cl;
     int vis = cl;
     if (p.causal) vis = min(max(qmax - c.kpos + 1, 0), cl);
@@ -212,11 +212,11 @@ __device__ __forceinline__ void cur_skip(const FwdParams& p, int rank, int qmax,
             c.lc = 0;
             ++c.t;
         }
-    } while (c.t < p.P && !cur_seg(p, rank, qmax, c));
+    } while (c.t < p.step_hi && !cur_seg(p, rank, qmax, c));
 }
 
 __device__ __forceinline__ void cur_first(const FwdParams& p, int rank, int qmax, KvCur& c) {
-    c.t = 0;
+    c.t = p.step_lo;
     c.lc = 0;
     if (!cur_seg(p, rank, qmax, c)) cur_skip(p, rank, qmax, c);
 }
@@ -247,7 +247,7 @@ __device__ __forceinline__ void cur_advance(const FwdParams& p, int rank, int qm
 __device__ __forceinline__ int cur_count(const FwdParams& p, int rank, int qmax) {
     KvCur c;
     int n = 0;
-    for (c.t = 0; c.t < p.P; ++c.t)
+    for (c.t = p.step_lo; c.t < p.step_hi; ++c.t)
         for (c.lc = 0; c.lc < p.chunks_per_rank; ++c.lc)
             if (cur_seg(p, rank, qmax, c)) n += c.tl + 1;
     return n;
@@ -341,8 +341,8 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdParams p) {
 
     const int64_t row_stride = (int64_t)p.Hkv * D;
     const uint32_t row_bytes = (uint32_t)(row_stride * 2);
-    const uint16_t* Kg = (const uint16_t*)p.K + ((int64_t)qt.b * p.S * p.Hkv + qt.kvh) * D;
-    const uint16_t* Vg = (const uint16_t*)p.V + ((int64_t)qt.b * p.S * p.Hkv + qt.kvh) * D;
+    const uint16_t* Kg = (const uint16_t*)p.K + ((int64_t)qt.b * p.kv_rows * p.Hkv + qt.kvh) * D;
+    const uint16_t* Vg = (const uint16_t*)p.V + ((int64_t)qt.b * p.kv_rows * p.Hkv + qt.kvh) * D;
     const typename T::Offs offs = T::offsets(w, lane, row_bytes);
 
     // ---- prologue: tiles 0 and 1 on their way into buffers 0 and 1; the V
@@ -551,22 +551,45 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdParams p) {
         }
     }
 
-    // ---- finalize: O = O / l, LSE = m + ln l (natural log)
+    // ---- finalize: O = O / l, LSE = m + ln l (natural log); with a running
+    // state, fold this result into it (lesson 8 section 3, whole blocks):
+    // O = (a O_old + b O_new) / (a + b), a = e^(lse_old - M), b = e^(lse - M)
     const float l_tot = halves_sum(l_run);
     const float lr_tot = halves_sum(lr_run);
-    const float inv = lr_tot > 0.f ? 1.f / lr_tot : 0.f;
+    float inv = lr_tot > 0.f ? 1.f / lr_tot : 0.f;
+    float lse = l_tot > 0.f ? (m_ref + __log2f(l_tot)) * kLn2 : kNegInf;
     if (qi < qt.rows) {
-        // a split writes its partial into its own slice of the partial buffers
         const int64_t obase = ((qt.b * p.q_rows + qt.q_row0 + qi) * p.Hq + qt.qh) * (int64_t)D +
                               (int64_t)split * p.o_split_stride;
+        const int64_t lidx = ((int64_t)qt.b * p.Hq + qt.qh) * p.q_rows + qt.q_row0 + qi +
+                             (int64_t)split * p.l_split_stride;
+        float w_old = 0.f;
+        if (p.fold) {
+            const float lse_old = p.LSE[lidx];
+            const float M = fmaxf(lse_old, lse);
+            if (M != kNegInf) {
+                const float a = __expf(lse_old - M), b = __expf(lse - M);
+                const float rw = 1.f / (a + b);
+                w_old = a * rw;
+                inv *= b * rw;
+                lse = M + __logf(a + b);
+            }
+        }
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
                 // accumulator registers 4*g4..4*g4+3 hold dims db*32 + 8*g4 + 4h + 0..3
                 const int dim = db * 32 + 8 * g4 + 4 * h;
-                const float o0 = oacc[db][4 * g4 + 0] * inv, o1 = oacc[db][4 * g4 + 1] * inv;
-                const float o2 = oacc[db][4 * g4 + 2] * inv, o3 = oacc[db][4 * g4 + 3] * inv;
+                float o0 = oacc[db][4 * g4 + 0] * inv, o1 = oacc[db][4 * g4 + 1] * inv;
+                float o2 = oacc[db][4 * g4 + 2] * inv, o3 = oacc[db][4 * g4 + 3] * inv;
+                if (p.fold) {
+                    const float4 old = *(const float4*)((const float*)p.O + obase + dim);
+                    o0 = __builtin_fmaf(w_old, old.x, o0);
+                    o1 = __builtin_fmaf(w_old, old.y, o1);
+                    o2 = __builtin_fmaf(w_old, old.z, o2);
+                    o3 = __builtin_fmaf(w_old, old.w, o3);
+                }
                 if (p.o_f32) {
                     *(float4*)((float*)p.O + obase + dim) = make_float4(o0, o1, o2, o3);
                 } else {
@@ -577,11 +600,9 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdParams p) {
                     *(uint2*)((uint16_t*)p.O + obase + dim) = make_uint2(w0, w1);
                 }
             }
-        if (h == 0) {
-            const float lse = l_tot > 0.f ? (m_ref + __log2f(l_tot)) * kLn2 : kNegInf;
-            p.LSE[((int64_t)qt.b * p.Hq + qt.qh) * p.q_rows + qt.q_row0 + qi +
-                  (int64_t)split * p.l_split_stride] = lse;
-        }
+        // the new LSE depends on the old one, so the load above has returned
+        // for every lane of the wave before this store issues
+        if (h == 0) p.LSE[lidx] = lse;
     }
 }
 

@@ -39,8 +39,8 @@ __global__ __launch_bounds__(NT) void fwd_f32_kernel(FwdParams p) {
     float m_run = kNegInf, l_run = 0.f;
 
     const int64_t row_stride = (int64_t)p.Hkv * D;
-    const float* Kg = (const float*)p.K + ((int64_t)qt.b * p.S * p.Hkv + qt.kvh) * D;
-    const float* Vg = (const float*)p.V + ((int64_t)qt.b * p.S * p.Hkv + qt.kvh) * D;
+    const float* Kg = (const float*)p.K + ((int64_t)qt.b * p.kv_rows * p.Hkv + qt.kvh) * D;
+    const float* Vg = (const float*)p.V + ((int64_t)qt.b * p.kv_rows * p.Hkv + qt.kvh) * D;
 
     // this work-group's key range: tiles [i0, i0 + cnt) of the visiting order
     const int n_all = kv_count(p, qt.rank, qmax, BN);
@@ -102,16 +102,30 @@ __global__ __launch_bounds__(NT) void fwd_f32_kernel(FwdParams p) {
     }
 
     if (qvalid) {
-        const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+        float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+        float lse = l_run > 0.f ? m_run * kLn2 + __logf(l_run) : kNegInf;
         float* Op = (float*)p.O + ((qt.b * p.q_rows + qt.q_row0 + qi) * p.Hq + qt.qh) * (int64_t)D +
                     (int64_t)split * p.o_split_stride;
-#pragma unroll
-        for (int e = 0; e < DP; ++e) Op[4 * e + part] = o[e] * inv;
-        if (part == 0) {
-            const float lse = l_run > 0.f ? m_run * kLn2 + __logf(l_run) : kNegInf;
-            p.LSE[((int64_t)qt.b * p.Hq + qt.qh) * p.q_rows + qt.q_row0 + qi +
-                  (int64_t)split * p.l_split_stride] = lse;
+        float* Lp = p.LSE + ((int64_t)qt.b * p.Hq + qt.qh) * p.q_rows + qt.q_row0 + qi +
+                    (int64_t)split * p.l_split_stride;
+        float w_old = 0.f;
+        if (p.fold) {  // fold into the running state (lesson 8 section 3, whole blocks)
+            const float lse_old = *Lp;
+            const float M = fmaxf(lse_old, lse);
+            if (M != kNegInf) {
+                const float a = __expf(lse_old - M), b = __expf(lse - M);
+                w_old = a / (a + b);
+                inv *= b / (a + b);
+                lse = M + __logf(a + b);
+            }
         }
+#pragma unroll
+        for (int e = 0; e < DP; ++e)
+            Op[4 * e + part] = p.fold ? __builtin_fmaf(w_old, Op[4 * e + part], o[e] * inv) : o[e] * inv;
+        // all four threads of the query read the old LSE before the one that
+        // writes it: the threads of a query are lanes of one wave, and the
+        // store depends on the loaded value
+        if (part == 0) *Lp = lse;
     }
 }
 

@@ -143,7 +143,7 @@ __device__ __forceinline__ void kv_seg(const FwdParams& p, int rank, int64_t qma
                                        KvIter& it) {
     int s = rank - it.t;
     if (s < 0) s += p.P;
-    it.krow = (int64_t)s * p.n + (int64_t)it.lc * p.c;
+    it.krow = (p.kv_block ? 0 : (int64_t)s * p.n) + (int64_t)it.lc * p.c;
     it.kpos = p.striped ? (int64_t)(s > rank)
                         : (int64_t)global_chunk(p.P, p.chunks_per_rank, s, it.lc) * p.c;
     int64_t vis = p.c;
@@ -157,14 +157,14 @@ __device__ __forceinline__ void kv_seg(const FwdParams& p, int rank, int64_t qma
 
 __device__ __forceinline__ bool kv_first(const FwdParams& p, int rank, int64_t qmax, int bn,
                                          KvIter& it) {
-    it.t = 0;
+    it.t = p.step_lo;
     it.lc = 0;
     it.tile = 0;
     kv_seg(p, rank, qmax, bn, it);
     while (it.tile >= it.ntiles) {
         if (++it.lc == p.chunks_per_rank) {
             it.lc = 0;
-            if (++it.t == p.P) return false;
+            if (++it.t == p.step_hi) return false;
         }
         kv_seg(p, rank, qmax, bn, it);
     }
@@ -175,7 +175,7 @@ __device__ __forceinline__ bool kv_first(const FwdParams& p, int rank, int64_t q
 __device__ __forceinline__ int kv_count(const FwdParams& p, int rank, int64_t qmax, int bn) {
     KvIter it;
     int n = 0;
-    for (it.t = 0; it.t < p.P; ++it.t)
+    for (it.t = p.step_lo; it.t < p.step_hi; ++it.t)
         for (it.lc = 0; it.lc < p.chunks_per_rank; ++it.lc) {
             kv_seg(p, rank, qmax, bn, it);
             n += it.ntiles;
@@ -189,7 +189,7 @@ __device__ __forceinline__ bool kv_next(const FwdParams& p, int rank, int64_t qm
     while (it.tile >= it.ntiles) {
         if (++it.lc == p.chunks_per_rank) {
             it.lc = 0;
-            if (++it.t == p.P) return false;
+            if (++it.t == p.step_hi) return false;
         }
         it.tile = 0;
         kv_seg(p, rank, qmax, bn, it);

@@ -23,11 +23,12 @@ namespace ra {
 // one per row inside a chunk.
 struct FwdParams {
     const void* Q;     // [B, q_rows, Hq, d]
-    const void* K;     // [B, S, Hkv, d], sharded order
-    const void* V;     // [B, S, Hkv, d], sharded order
+    const void* K;     // [B, S, Hkv, d], sharded order (kv_block: [B, n, Hkv, d])
+    const void* V;     // same as K
     void* O;           // [B, q_rows, Hq, d]
     float* LSE;        // [B, Hq, q_rows]
     int64_t S;         // total tokens (all shards)
+    int64_t kv_rows;   // rows per batch entry of K/V: S, or n for a block
     int64_t n;         // tokens per shard, S / P
     int64_t c;         // tokens per chunk: n / chunks_per_rank
     int64_t q_rows;    // rows of Q/O/LSE: S for all ranks, n for one rank
@@ -48,6 +49,13 @@ struct FwdParams {
     // its (O, LSE) partial at offsets s * o_split_stride / s * l_split_stride.
     int kv_splits;
     int64_t o_split_stride, l_split_stride;
+    // Ring steps visited: t in [step_lo, step_hi) (0 and P for a whole pass).
+    // kv_block = 1: K/V hold only the shard of step step_lo, [B, n, Hkv, d]
+    // (a received block), instead of all P shards.  fold = 1: O (fp32) and
+    // LSE hold a running state that this launch's result is folded into.
+    int step_lo, step_hi;
+    int kv_block;
+    int fold;
     float scale_log2;  // log2(e) / sqrt(d)
     float scale;       // 1 / sqrt(d)
 };

@@ -161,3 +161,21 @@ def test_fwd_workspace_bytes():
         f(1, 8, 8, 8200, 128, 8, False, True, "zigzag", 1, 0)
     with pytest.raises(ra.RaError):
         f(1, 8, 8, 8192, 128, 8, False, True, "zigzag", 1, 65)
+
+
+def test_ring_step_rejects_before_the_device():
+    L = ra.lib()
+
+    def call(t=0, rank=0, **kw):
+        a = dict(B=1, Hq=8, Hkv=8, S=8192, d=128, P=8, causal=1, layout=1, dtype=1)
+        a.update(kw)
+        return L.ra_ring_step(FAKE, FAKE, FAKE, FAKE, FAKE, a["B"], a["Hq"], a["Hkv"], a["S"], a["d"],
+                              a["P"], rank, t, a["causal"], a["layout"], a["dtype"], NULL)
+
+    assert call(t=8) == ra.RA_ERR_INVALID_ARG
+    assert call(t=-1) == ra.RA_ERR_INVALID_ARG
+    assert call(rank=8) == ra.RA_ERR_INVALID_ARG
+    assert call(layout=5) == ra.RA_ERR_INVALID_ARG
+    assert call(S=8200) == ra.RA_ERR_UNSUPPORTED
+    assert call(d=80) == ra.RA_ERR_UNSUPPORTED
+    assert call(Hq=6, Hkv=4) == ra.RA_ERR_UNSUPPORTED

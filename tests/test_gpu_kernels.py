@@ -9,7 +9,8 @@ import torch
 
 import long_context_exact_amd as ra
 import oracle
-from gpu_helpers import (check, fmt, from_dev, log, qkv, scale_bf16, shard, to_dev, unshard)
+from gpu_helpers import (BF16_O_MAX, F32_O_MAX, check, fmt, from_dev, log, qkv, scale_bf16, shard,
+                         to_dev, unshard)
 
 pytestmark = pytest.mark.gpu
 
@@ -334,3 +335,104 @@ def test_prefill_auto_splits_fall_back_to_smaller_workspace():
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
     check(from_dev(outs[2][0]), O_ref, from_dev(outs[2][1]), lse_ref, "bf16", "no workspace")
     check(from_dev(outs[0][0]), O_ref, from_dev(outs[0][1]), lse_ref, "bf16", "two ranges")
+
+
+RING = [  # B, S, Hq, Hkv, d, P, layout, causal, dtype
+    (2, 640, 4, 2, 128, 4, "zigzag", True, "bf16"),
+    (1, 1024, 2, 2, 64, 8, "contiguous", True, "bf16"),
+    (1, 1040, 4, 2, 128, 4, "striped", True, "bf16"),
+    (1, 1200, 2, 1, 128, 5, "zigzag", False, "bf16"),
+    (1, 520, 4, 2, 64, 4, "zigzag", True, "f32"),
+    (1, 768, 2, 2, 128, 3, "zigzag4", True, "f32"),
+]
+
+
+def _ring_rank(Qs, Ks, Vs, S, P, r, causal, layout, order=None):
+    """Run rank r's P steps, each on a copy of the arriving block only."""
+    B, _, Hq, d = Qs.shape
+    n = S // P
+    Qr = Qs[:, r * n:(r + 1) * n].contiguous()
+    O = torch.empty(B, n, Hq, d, dtype=torch.float32, device="cuda")
+    L = torch.empty(B, Hq, n, dtype=torch.float32, device="cuda")
+    for t in (order or range(P)):
+        s = (r - t) % P
+        Kb = Ks[:, s * n:(s + 1) * n].contiguous()
+        Vb = Vs[:, s * n:(s + 1) * n].contiguous()
+        ra.ra_ring_step(Qr, Kb, Vb, O, L, S, P, r, t, causal, layout)
+    torch.cuda.synchronize()
+    return O, L
+
+
+@pytest.mark.parametrize("case", RING, ids=[_id(c) for c in RING])
+def test_ring_step_fold(case):
+    """P calls of ra_ring_step, each seeing only the block that has arrived,
+    reach the oracle's result (and ra_fwd_rank's within rounding); the steps
+    after t = 0 may come in any order."""
+    B, S, Hq, Hkv, d, P, layout, causal, dtype = case
+    log(f"ring steps {_id(case)}")
+    Qn, Kn, Vn = qkv(B, S, S, Hq, Hkv, d, dtype, (1300, S, P))
+    (Qs, Ks, Vs), O_all, L_all = _run_prefill(Qn, Kn, Vn, P, layout, causal, dtype)
+    O_ref, lse_ref = oracle.attention(Qn, Kn, Vn, causal)
+    n = S // P
+    O_g = torch.empty_like(O_all)
+    L_g = torch.empty_like(L_all)
+    for r in range(P):
+        O, L = _ring_rank(Qs, Ks, Vs, S, P, r, causal, layout)
+        O_g[:, r * n:(r + 1) * n] = O
+        L_g[:, :, r * n:(r + 1) * n] = L
+    e = check(unshard(from_dev(O_g), S, P, layout, axis=1), O_ref,
+              unshard(from_dev(L_g), S, P, layout, axis=2), lse_ref, dtype, _id(case))
+    log(f"  ok {fmt(e)}")
+    # the two GPU paths round differently (each step normalises its own bf16
+    # P); both meet the oracle bar above, and agree within it
+    tol = BF16_O_MAX if dtype == "bf16" else F32_O_MAX
+    assert (O_g - O_all).abs().max().item() <= tol
+    fin = torch.isfinite(L_all)
+    assert torch.equal(torch.isfinite(L_g), fin)
+    assert (L_g[fin] - L_all[fin]).abs().max().item() <= tol
+    # t = 0 first, the rest reversed
+    r = P - 1
+    O2, L2 = _ring_rank(Qs, Ks, Vs, S, P, r, causal, layout, order=[0] + list(range(P - 1, 0, -1)))
+    assert (O2 - O_g[:, r * n:(r + 1) * n]).abs().max().item() <= tol
+    assert (L2 - L_g[:, :, r * n:(r + 1) * n]).abs().max().item() <= tol
+
+
+def test_ring_step_double_buffered_streams():
+    """The schedule a multi-GPU ring would run: while step t computes on one
+    receive buffer, the next block is copied into the other on a second
+    stream (standing in for the peer-to-peer receive), ordered by events.
+    The result equals the single-stream loop bit for bit."""
+    B, S, Hq, Hkv, d, P, layout = 1, 2048, 8, 2, 128, 4, "zigzag"
+    Qn, Kn, Vn = qkv(B, S, S, Hq, Hkv, d, "bf16", (1301,))
+    (Qs, Ks, Vs), _, _ = _run_prefill(Qn, Kn, Vn, P, layout, True, "bf16")
+    n = S // P
+    r = 1
+    ref_O, ref_L = _ring_rank(Qs, Ks, Vs, S, P, r, True, layout)
+    comp = torch.cuda.current_stream()
+    copy = torch.cuda.Stream()
+    Qr = Qs[:, r * n:(r + 1) * n].contiguous()
+    bufK = [torch.empty(B, n, Hkv, d, dtype=Ks.dtype, device="cuda") for _ in range(2)]
+    bufV = [torch.empty_like(bufK[0]) for _ in range(2)]
+    arrived = [torch.cuda.Event() for _ in range(2)]
+    free = [torch.cuda.Event() for _ in range(2)]
+    O = torch.empty(B, n, Hq, d, dtype=torch.float32, device="cuda")
+    L = torch.empty(B, Hq, n, dtype=torch.float32, device="cuda")
+
+    def receive(t):
+        s = (r - t) % P
+        with torch.cuda.stream(copy):
+            if t >= 2:
+                copy.wait_event(free[t % 2])
+            bufK[t % 2].copy_(Ks[:, s * n:(s + 1) * n])
+            bufV[t % 2].copy_(Vs[:, s * n:(s + 1) * n])
+            arrived[t % 2].record(copy)
+
+    receive(0)
+    for t in range(P):
+        if t + 1 < P:
+            receive(t + 1)
+        comp.wait_event(arrived[t % 2])
+        ra.ra_ring_step(Qr, bufK[t % 2], bufV[t % 2], O, L, S, P, r, t, True, layout)
+        free[t % 2].record(comp)
+    torch.cuda.synchronize()
+    assert torch.equal(O, ref_O) and torch.equal(L, ref_L)
