@@ -118,6 +118,10 @@ def main() -> int:
     ap.add_argument("--all-ranks", action="store_true",
                     help="also time every rank's share of the prefill (the ring step lasts as "
                          "long as the slowest rank)")
+    ap.add_argument("--decode-rr-block", type=int, default=0,
+                    help="decode over the KV cache dealt round-robin in blocks of this many tokens "
+                         "to the 8 shard caches (built by ra_kv_append_rr before timing); 0 = one "
+                         "contiguous cache per sequence (default)")
     ap.add_argument("--ring-steps", action="store_true",
                     help="also time the timed rank's share as P ring steps (ra_ring_step) on one "
                          "stream, and double-buffered with the next block copied on a second stream")
@@ -207,8 +211,23 @@ def main() -> int:
         Od = torch.empty(rows, wd.d, dtype=torch.float32, device=dev)
         ld = torch.empty(rows, dtype=torch.float32, device=dev)
 
-        def decode():
-            ra.ra_attn_partial(Qd, Kd, Vd, Op, lp, parts)
+        rr = args.decode_rr_block
+        if rr > 0:
+            # the cache a KV-parallel group builds by appending blocks in turn
+            cap = max(len(range(sh * rr, wd.S, wd.P * rr)) * rr for sh in range(wd.P)) + rr
+            Kc = torch.empty(wd.P, wd.B, cap, wd.Hkv, wd.d, dtype=torch.bfloat16, device=dev)
+            Vc = torch.empty_like(Kc)
+            ra.ra_kv_append_rr(Kc, Vc, Kd, Vd, 0, rr)
+            del Kd, Vd
+            torch.cuda.synchronize()
+            if parts % wd.P:
+                raise SystemExit("--decode-parts must be a multiple of the 8 shards")
+
+            def decode():
+                ra.ra_attn_partial_rr(Qd, Kc, Vc, Op, lp, wd.S, rr, parts // wd.P)
+        else:
+            def decode():
+                ra.ra_attn_partial(Qd, Kd, Vd, Op, lp, parts)
 
         def merge():
             ra.ra_merge_partials(Op, lp, Od, ld)
@@ -285,6 +304,20 @@ def main() -> int:
                                       "ms_min": mn["decode"]},
                          "merge_ms": ms["merge"], "parts": args.decode_parts}
         cfg["decode_workload"] = wd.name
+        if rr > 0:
+            # one decode step's append: one new token per sequence
+            newK = torch.zeros(wd.B, 1, wd.Hkv, wd.d, dtype=torch.bfloat16, device=dev)
+            for _ in range(args.warmup):
+                ra.ra_kv_append_rr(Kc, Vc, newK, newK, wd.S, rr)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(args.steps):
+                ra.ra_kv_append_rr(Kc, Vc, newK, newK, wd.S, rr)
+            e1.record()
+            torch.cuda.synchronize()
+            out["decode"]["cache"] = {"layout": f"round-robin blocks of {rr} tokens over {wd.P} shards",
+                                      "append_one_token_ms": e0.elapsed_time(e1) / args.steps}
+            cfg["decode_workload"] = f"{wd.name} round-robin cache (blocks of {rr})"
         if not do_pre:
             out.update({"value": tot, "unit": "GB/s", "roofline": out["decode"]["roofline"]})
             cfg["workload"] = wd.name

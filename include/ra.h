@@ -231,6 +231,42 @@ int ra_attn_partial(const void* Q, const void* K, const void* V, float* O_parts,
                     int d, int n_parts, int dtype, void* stream);
 
 /*
+ * Round-robin KV cache of a KV-parallel group ([HX]: new tokens' KV is
+ * written to the devices of the group in turn, one block of tokens each, so
+ * every device's cache grows evenly).  Key x of a sequence is in block
+ * j = x / block, held by shard j mod P at shard-local row
+ * (j / P) * block + x mod block.  The P shard caches are one tensor
+ * [P, B, cap, Hkv, d] (dtype), shard-major, so each shard's cache is one
+ * contiguous region as it would be on its own device.
+ *
+ * ra_kv_append_rr -- write the K/V of n_new new tokens at sequence positions
+ * len .. len+n_new-1 into their shards.
+ *   K_new, V_new  [B, n_new, Hkv, d]; K_cache, V_cache as above.
+ * Rows of other positions are not touched.  All pointers 16-byte aligned.
+ * Requirements: len >= 0, n_new >= 1, block >= 1, every shard's length after
+ * the append <= cap (shard 0 is the longest), d in {64, 128}.
+ */
+int ra_kv_append_rr(void* K_cache, void* V_cache, const void* K_new, const void* V_new,
+                    int B, int Hkv, int d, int P, int64_t cap, int64_t len, int64_t n_new,
+                    int64_t block, int dtype, void* stream);
+
+/*
+ * ra_attn_partial_rr -- ra_attn_partial over the round-robin cache of a
+ * sequence of `len` keys: every shard is cut into parts_per_shard parts of
+ * its own length, part p*parts_per_shard + j covering the j-th range of shard
+ * p ([HX] phase 1: each device computes partials over its own cache).
+ *   Q [B, Sq, Hq, d]; O_parts [P*parts_per_shard, B*Sq*Hq, d] fp32;
+ *   lse_parts [P*parts_per_shard, B*Sq*Hq] fp32.
+ * ra_merge_partials over all P*parts_per_shard parts gives the attention of
+ * the queries over all len keys.  Requirements as ra_attn_partial, plus
+ * len >= 1, block >= 1, the shards' lengths <= cap.
+ */
+int ra_attn_partial_rr(const void* Q, const void* K_cache, const void* V_cache, float* O_parts,
+                       float* lse_parts, int B, int Hq, int Hkv, int64_t Sq, int64_t cap,
+                       int64_t len, int64_t block, int P, int parts_per_shard, int d, int dtype,
+                       void* stream);
+
+/*
  * ra_layout_gather -- move a sequence tensor between natural order and
  * sharded order ([L8] section 4B and exercise: the zig-zag chunk maps; the
  * striped token map).

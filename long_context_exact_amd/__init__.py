@@ -28,7 +28,7 @@ def layout_zigzag_k(k: int) -> int:
 DTYPE_F32, DTYPE_BF16 = 0, 1
 
 EXPORTS = ("ra_fwd_rank", "ra_fwd_all", "ra_fwd_rank_ws", "ra_fwd_all_ws", "ra_fwd_workspace_bytes",
-           "ra_ring_step",
+           "ra_ring_step", "ra_kv_append_rr", "ra_attn_partial_rr",
            "ra_merge_partials", "ra_attn_partial",
            "ra_layout_gather", "ra_last_error", "ra_version")
 
@@ -61,11 +61,15 @@ def lib() -> ctypes.CDLL:
         L.ra_fwd_workspace_bytes.argtypes = [i32, i32, i32, i64, i32, i32, i32, i32, i32, i32, i32]
         L.ra_ring_step.argtypes = [vp, vp, vp, fp, fp, i32, i32, i32, i64, i32, i32, i32, i32, i32,
                                    i32, i32, vp]
+        L.ra_kv_append_rr.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i64, i64, i64, i64, i32, vp]
+        L.ra_attn_partial_rr.argtypes = [vp, vp, vp, fp, fp, i32, i32, i32, i64, i64, i64, i64, i32,
+                                         i32, i32, i32, vp]
         L.ra_fwd_workspace_bytes.restype = ctypes.c_int64
         L.ra_merge_partials.argtypes = [fp, fp, vp, fp, i32, i64, i32, i32, vp]
         L.ra_attn_partial.argtypes = [vp, vp, vp, fp, fp, i32, i32, i32, i64, i64, i32, i32, i32, vp]
         L.ra_layout_gather.argtypes = [vp, vp, i64, i64, i64, i32, i32, i32, vp]
         for f in ("ra_fwd_rank", "ra_fwd_all", "ra_fwd_rank_ws", "ra_fwd_all_ws", "ra_ring_step",
+                  "ra_kv_append_rr", "ra_attn_partial_rr",
                   "ra_merge_partials", "ra_attn_partial", "ra_layout_gather"):
             getattr(L, f).restype = ctypes.c_int
         L.ra_last_error.restype = ctypes.c_char_p
@@ -235,6 +239,47 @@ def ra_ring_step(Q_r, K_blk, V_blk, O_acc, LSE_acc, S: int, P: int, rank: int, t
                               _dev(O_acc, "O_acc"), _dev(LSE_acc, "LSE_acc"), B, Hq, Hkv, S, d, P,
                               rank, t, int(bool(causal)), _layout(layout), _dtype_code(Q_r),
                               _stream(stream)))
+
+
+def ra_kv_append_rr(K_cache, V_cache, K_new, V_new, length: int, block: int, stream=None):
+    """Append new tokens' K/V ([B, n_new, Hkv, d]) at positions length ..
+    length+n_new-1 to the round-robin shard caches K_cache, V_cache
+    [P, B, cap, Hkv, d]."""
+    P, B, cap, Hkv, d = K_cache.shape
+    if V_cache.shape != K_cache.shape or K_new.shape != V_new.shape:
+        raise ValueError("shape mismatch")
+    if K_new.shape[0] != B or tuple(K_new.shape[2:]) != (Hkv, d):
+        raise ValueError("new K/V must be [B, n_new, Hkv, d]")
+    if not (K_cache.dtype == V_cache.dtype == K_new.dtype == V_new.dtype):
+        raise TypeError("caches and new rows must share a dtype")
+    _check(lib().ra_kv_append_rr(_dev(K_cache, "K_cache"), _dev(V_cache, "V_cache"),
+                                 _dev(K_new, "K_new"), _dev(V_new, "V_new"), B, Hkv, d, P, cap,
+                                 int(length), K_new.shape[1], int(block), _dtype_code(K_new),
+                                 _stream(stream)))
+
+
+def ra_attn_partial_rr(Q, K_cache, V_cache, O_parts, lse_parts, length: int, block: int,
+                       parts_per_shard: int, stream=None):
+    """Per-part partials of Q [B, Sq, Hq, d] over the round-robin shard caches
+    [P, B, cap, Hkv, d] holding `length` keys: O_parts [P*parts_per_shard,
+    B*Sq*Hq, d], lse_parts [P*parts_per_shard, B*Sq*Hq], both float32."""
+    P, B, cap, Hkv, d = K_cache.shape
+    Sq, Hq = Q.shape[1], Q.shape[2]
+    n_parts = P * parts_per_shard
+    rows = B * Sq * Hq
+    torch = _torch()
+    if tuple(Q.shape) != (B, Sq, Hq, d) or V_cache.shape != K_cache.shape:
+        raise ValueError("shape mismatch")
+    if tuple(O_parts.shape) != (n_parts, rows, d) or tuple(lse_parts.shape) != (n_parts, rows):
+        raise ValueError("partials must be [P*parts_per_shard, B*Sq*Hq, (d)]")
+    if O_parts.dtype != torch.float32 or lse_parts.dtype != torch.float32:
+        raise TypeError("partials must be float32")
+    if not (K_cache.dtype == V_cache.dtype == Q.dtype):
+        raise TypeError("Q, K, V must share a dtype")
+    _check(lib().ra_attn_partial_rr(_dev(Q, "Q"), _dev(K_cache, "K_cache"), _dev(V_cache, "V_cache"),
+                                    _dev(O_parts, "O_parts"), _dev(lse_parts, "lse_parts"), B, Hq,
+                                    Hkv, Sq, cap, int(length), int(block), P, int(parts_per_shard),
+                                    d, _dtype_code(Q), _stream(stream)))
 
 
 def ra_merge_partials(O_parts, lse_parts, O, lse=None, stream=None):

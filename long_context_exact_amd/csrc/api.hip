@@ -6,7 +6,7 @@
 #include <stdio.h>
 
 #include "../../include/ra.h"
-#include "ra_internal.h"
+#include "ra_device.h"
 
 namespace {
 
@@ -342,13 +342,86 @@ int ra_attn_partial(const void* Q, const void* K, const void* V, float* O_parts,
     p.lse_parts = lse_parts;
     p.Sq = Sq;
     p.Skv = Skv;
-    p.part_len = (Skv + n_parts - 1) / n_parts;
+    p.kv_cap = Skv;
+    p.rr_block = 0;
     p.B = B;
     p.Hq = Hq;
     p.Hkv = Hkv;
     p.G = Hq / Hkv;
     p.n_parts = n_parts;
-    p.splits = 1;
+    p.n_shards = 1;
+    p.parts_per_shard = n_parts;
+    p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d));
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = dtype == RA_DTYPE_BF16 ? ra::launch_decode_bf16(p, d, s) : ra::launch_decode_f32(p, d, s);
+    return hip_status(e, "decode kernel launch");
+}
+
+int ra_kv_append_rr(void* K_cache, void* V_cache, const void* K_new, const void* V_new, int B,
+                    int Hkv, int d, int P, int64_t cap, int64_t len, int64_t n_new, int64_t block,
+                    int dtype, void* stream) {
+    if (!K_cache || !V_cache || !K_new || !V_new) return fail(RA_ERR_INVALID_ARG, "null tensor pointer");
+    if (B <= 0 || Hkv <= 0 || P <= 0 || cap <= 0 || n_new <= 0 || block <= 0 || len < 0)
+        return fail(RA_ERR_INVALID_ARG, "sizes must be positive (len >= 0)");
+    if (dtype != RA_DTYPE_F32 && dtype != RA_DTYPE_BF16)
+        return fail(RA_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+    if (d != 64 && d != 128) return fail(RA_ERR_UNSUPPORTED, "head dim %d (supported: 64, 128)", d);
+    if (P > 4096) return fail(RA_ERR_UNSUPPORTED, "P=%d exceeds 4096", P);
+    // shard 0 receives the first block of every round, so it is never shorter
+    const int64_t need = ra::rr_shard_len(len + n_new, block, P, 0);
+    if (need > cap)
+        return fail(RA_ERR_INVALID_ARG, "shard 0 would hold %lld rows, capacity %lld", (long long)need,
+                    (long long)cap);
+    if ((int64_t)B * n_new > 0x7fffffffLL) return fail(RA_ERR_UNSUPPORTED, "too many new rows");
+    if (((uintptr_t)K_cache | (uintptr_t)V_cache | (uintptr_t)K_new | (uintptr_t)V_new) % 16 != 0)
+        return fail(RA_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
+    const int64_t row_bytes = (int64_t)Hkv * d * (dtype == RA_DTYPE_BF16 ? 2 : 4);
+    return hip_status(ra::launch_kv_append_rr(K_cache, V_cache, K_new, V_new, B, row_bytes, P, cap,
+                                              len, n_new, block, (hipStream_t)stream),
+                      "append kernel launch");
+}
+
+int ra_attn_partial_rr(const void* Q, const void* K_cache, const void* V_cache, float* O_parts,
+                       float* lse_parts, int B, int Hq, int Hkv, int64_t Sq, int64_t cap,
+                       int64_t len, int64_t block, int P, int parts_per_shard, int d, int dtype,
+                       void* stream) {
+    if (!Q || !K_cache || !V_cache || !O_parts || !lse_parts)
+        return fail(RA_ERR_INVALID_ARG, "null tensor pointer");
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || Sq <= 0 || cap <= 0 || len <= 0 || block <= 0 || P <= 0 ||
+        parts_per_shard <= 0)
+        return fail(RA_ERR_INVALID_ARG, "sizes must be positive");
+    if (dtype != RA_DTYPE_F32 && dtype != RA_DTYPE_BF16)
+        return fail(RA_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+    if (d != 64 && d != 128) return fail(RA_ERR_UNSUPPORTED, "head dim %d (supported: 64, 128)", d);
+    if (Hq % Hkv != 0) return fail(RA_ERR_UNSUPPORTED, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+    if (Sq * (Hq / Hkv) > 32)
+        return fail(RA_ERR_UNSUPPORTED, "Sq*(Hq/Hkv)=%lld exceeds 32 query rows per kv head",
+                    (long long)(Sq * (Hq / Hkv)));
+    if (P > 4096) return fail(RA_ERR_UNSUPPORTED, "P=%d exceeds 4096", P);
+    if (ra::rr_shard_len(len, block, P, 0) > cap)
+        return fail(RA_ERR_INVALID_ARG, "%lld keys in blocks of %lld exceed shard capacity %lld",
+                    (long long)len, (long long)block, (long long)cap);
+    const int64_t n_parts = (int64_t)P * parts_per_shard;
+    const int64_t grid = (int64_t)B * Hkv * n_parts;
+    if (n_parts > 0x7fffffffLL || grid > 0x7fffffffLL)
+        return fail(RA_ERR_UNSUPPORTED, "grid of %lld work-groups", (long long)grid);
+    ra::DecodeParams p;
+    p.Q = Q;
+    p.K = K_cache;
+    p.V = V_cache;
+    p.O_parts = O_parts;
+    p.lse_parts = lse_parts;
+    p.Sq = Sq;
+    p.Skv = len;
+    p.kv_cap = cap;
+    p.rr_block = block;
+    p.B = B;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.G = Hq / Hkv;
+    p.n_parts = (int)n_parts;
+    p.n_shards = P;
+    p.parts_per_shard = parts_per_shard;
     p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d));
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = dtype == RA_DTYPE_BF16 ? ra::launch_decode_bf16(p, d, s) : ra::launch_decode_f32(p, d, s);

@@ -54,8 +54,8 @@ struct DecStage {
         for (int i = 0; i < LOADS; ++i) {
             const bool ok = row0 + i * (NT / KCH) < klen;
             const int64_t step = (int64_t)i * (NT / KCH) * row_stride;
-            r.k[i] = ok ? *(const uint4*)((const char*)(Kb + step) + off) : make_uint4(0, 0, 0, 0);
-            r.v[i] = ok ? *(const uint4*)((const char*)(Vb + step) + off) : make_uint4(0, 0, 0, 0);
+            r.k[i] = ok ? load_once16((const char*)(Kb + step) + off) : make_uint4(0, 0, 0, 0);
+            r.v[i] = ok ? load_once16((const char*)(Vb + step) + off) : make_uint4(0, 0, 0, 0);
         }
     }
     static __device__ __forceinline__ void store(const Regs& r, uint16_t* Ks, uint16_t* Vs, int t) {
@@ -101,15 +101,13 @@ __global__ __launch_bounds__(NT, 2) void decode_bf16_kernel(DecodeParams p) {
         }
     }
 
-    int64_t k0 = (int64_t)part * p.part_len;
-    int64_t k1 = k0 + p.part_len;
-    if (k1 > p.Skv) k1 = p.Skv;
-    if (k0 > k1) k0 = k1;
+    int64_t k0, k1, base;
+    decode_part(p, part, b, kvh, D, k0, k1, base);
     const int64_t nstages = (k1 - k0 + STAGE - 1) / STAGE;
 
     const int64_t row_stride = (int64_t)p.Hkv * D;
-    const uint16_t* Kg = (const uint16_t*)p.K + ((int64_t)b * p.Skv * p.Hkv + kvh) * D;
-    const uint16_t* Vg = (const uint16_t*)p.V + ((int64_t)b * p.Skv * p.Hkv + kvh) * D;
+    const uint16_t* Kg = (const uint16_t*)p.K + base;
+    const uint16_t* Vg = (const uint16_t*)p.V + base;
 
     f32x16 oacc[DB];
 #pragma unroll
@@ -281,13 +279,11 @@ __global__ __launch_bounds__(128) void decode_f32_kernel(DecodeParams p) {
         q[e] = valid ? qp[4 * e + part4] : 0.f;
         o[e] = 0.f;
     }
-    int64_t k0 = (int64_t)part * p.part_len;
-    int64_t k1 = k0 + p.part_len;
-    if (k1 > p.Skv) k1 = p.Skv;
-    if (k0 > k1) k0 = k1;
+    int64_t k0, k1, base;
+    decode_part(p, part, b, kvh, D, k0, k1, base);
     const int64_t row_stride = (int64_t)p.Hkv * D;
-    const float* Kg = (const float*)p.K + ((int64_t)b * p.Skv * p.Hkv + kvh) * D;
-    const float* Vg = (const float*)p.V + ((int64_t)b * p.Skv * p.Hkv + kvh) * D;
+    const float* Kg = (const float*)p.K + base;
+    const float* Vg = (const float*)p.V + base;
     float m_run = kNegInf, l_run = 0.f;
     for (int64_t kb = k0; kb < k1; kb += BK) {
         const int klen = (k1 - kb) < BK ? (int)(k1 - kb) : BK;

@@ -10,7 +10,10 @@
 // Pure data movement.  The chunked splits move whole chunks of c rows, so the
 // chunk kernel gives each work-group a contiguous byte range inside one chunk
 // and computes the source and destination chunk bases once (scalar
-// arithmetic); the threads then stream 16-byte units.  The striped split
+// arithmetic); the threads then stream 16-byte units, read with the
+// non-temporal hint (each byte is read once; measured on one box: 5.64 TB/s
+// for Q, K, V against 5.32 with plain loads and 5.57 with non-temporal loads
+// and stores).  The striped split
 // moves single rows: the row kernel gives each wave whole rows and maps each
 // destination row to its source once.  The general kernel (any alignment)
 // copies 16-, 4- or 1-byte units and maps every destination row to its source.
@@ -90,7 +93,7 @@ __global__ __launch_bounds__(256) void layout_chunks_kernel(ChunkArgs a) {
     uint4* d = (uint4*)(a.dst + o * a.seq_bytes + (int64_t)q * a.chunk_bytes + beg);
     const int units = (int)(len >> 4);
 #pragma unroll 4
-    for (int i = threadIdx.x; i < units; i += 256) d[i] = s[i];
+    for (int i = threadIdx.x; i < units; i += 256) d[i] = load_once16(s + i);
 }
 
 // Striped row copy: work-group -> (outer index o, ROWS consecutive
@@ -116,7 +119,7 @@ __global__ __launch_bounds__(256) void layout_rows_kernel(RowArgs a) {
         const unsigned sk = a.inverse ? (k % a.P) * a.n + k / a.P : (k % a.n) * a.P + k / a.n;
         const uint4* s = (const uint4*)(a.src + o * a.seq_bytes + (int64_t)sk * a.row_bytes);
         uint4* d = (uint4*)(a.dst + o * a.seq_bytes + (int64_t)k * a.row_bytes);
-        for (int i = lane; i < units; i += 64) d[i] = s[i];
+        for (int i = lane; i < units; i += 64) d[i] = load_once16(s + i);
     }
 }
 

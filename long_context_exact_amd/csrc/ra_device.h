@@ -25,8 +25,44 @@ __device__ __forceinline__ int swap_bits23(int m) {
     return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
 }
 
+// 16-byte load of data that is read once: the non-temporal hint keeps the
+// stream from displacing reused lines and reads HBM faster than a plain load
+// (measured on gfx950: 6.6-6.8 TB/s against 6.1-6.2 for a read-only stream).
+__device__ __forceinline__ uint4 load_once16(const void* p) {
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 v = __builtin_nontemporal_load((const u32x4*)p);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 __device__ __forceinline__ float xor32_max(float x) { return fmaxf(x, __shfl_xor(x, 32, 64)); }
 __device__ __forceinline__ float xor32_sum(float x) { return x + __shfl_xor(x, 32, 64); }
+
+// ----------------------------------------------------------------------------
+// Round-robin KV blocks (Helix article: new tokens' KV goes to the devices of
+// the KV-parallel group in turn, one block each).  Key x is in block
+// j = x / block, on shard j mod P, at local row (j / P) * block + x mod block.
+// With `total` keys, shard s holds the blocks s, s + P, ... below
+// ceil(total / block); only the last block of the sequence can be partial.
+// ----------------------------------------------------------------------------
+__host__ __device__ inline int64_t rr_shard_len(int64_t total, int64_t block, int P, int s) {
+    const int64_t nb = (total + block - 1) / block;
+    if (s >= nb) return 0;
+    int64_t len = ((nb - 1 - s) / P + 1) * block;
+    if ((nb - 1) % P == s) len -= nb * block - total;
+    return len;
+}
+
+// key range [k0, k1) (shard-local rows) and K/V element offset of one decode part
+__device__ __forceinline__ void decode_part(const DecodeParams& p, int part, int b, int kvh, int d,
+                                            int64_t& k0, int64_t& k1, int64_t& base) {
+    const int s = part / p.parts_per_shard, j = part % p.parts_per_shard;
+    const int64_t L = p.rr_block > 0 ? rr_shard_len(p.Skv, p.rr_block, p.n_shards, s) : p.Skv;
+    const int64_t plen = (L + p.parts_per_shard - 1) / p.parts_per_shard;
+    k0 = (int64_t)j * plen;
+    k1 = k0 + plen < L ? k0 + plen : L;
+    if (k0 > k1) k0 = k1;
+    base = (((int64_t)s * p.B + b) * p.kv_cap * p.Hkv + kvh) * d;
+}
 
 // ----------------------------------------------------------------------------
 // Chunk maps of the splits (lesson 8, section 4 and its exercise).

@@ -60,17 +60,25 @@ struct FwdParams {
     float scale;       // 1 / sqrt(d)
 };
 
+// Decode over a KV cache held as n_shards shard caches (one per device of a
+// KV-parallel group): row r of batch entry b of shard s sits at row
+// (s * B + b) * kv_cap + r of K and V.  One contiguous cache is one shard
+// with kv_cap = Skv.  Under round-robin blocks (rr_block > 0) key x of the
+// sequence lives in shard (x / rr_block) mod n_shards, so shard lengths
+// follow from Skv alone.  Each shard is cut into parts_per_shard parts.
 struct DecodeParams {
     const void* Q;     // [B, Sq, Hq, d]
-    const void* K;     // [B, Skv, Hkv, d]
+    const void* K;     // [n_shards, B, kv_cap, Hkv, d]
     const void* V;
     float* O_parts;    // [n_parts, B*Sq*Hq, d]
     float* lse_parts;  // [n_parts, B*Sq*Hq]
-    int64_t Sq, Skv;
-    int64_t part_len;  // ceil(Skv / n_parts)
+    int64_t Sq;
+    int64_t Skv;       // keys of the sequence (all shards)
+    int64_t kv_cap;    // rows per (shard, batch entry)
+    int64_t rr_block;  // 0: one contiguous cache; > 0: round-robin block size
     int B, Hq, Hkv, G;
-    int n_parts;
-    int splits;        // work-groups per part
+    int n_parts;       // n_shards * parts_per_shard
+    int n_shards, parts_per_shard;
     float scale_log2;
 };
 
@@ -95,6 +103,9 @@ hipError_t launch_fwd_f32(const FwdParams& p, int d, hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeParams& p, int d, hipStream_t s);
 hipError_t launch_decode_f32(const DecodeParams& p, int d, hipStream_t s);
 hipError_t launch_merge(const MergeParams& p, int d, hipStream_t s);
+hipError_t launch_kv_append_rr(void* K_cache, void* V_cache, const void* K_new, const void* V_new,
+                              int B, int64_t row_bytes, int P, int64_t cap, int64_t len,
+                              int64_t n_new, int64_t block, hipStream_t s);
 hipError_t launch_layout(const void* src, void* dst, int64_t outer, int64_t S, int64_t inner_bytes,
                          int P, int chunks_per_rank, int striped, int inverse, hipStream_t s);
 

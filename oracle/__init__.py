@@ -148,6 +148,20 @@ def natural_positions(S: int, P: int, layout: str) -> np.ndarray:
     return np.concatenate(pos)
 
 
+def helix_round_robin(total: int, block: int, P: int) -> list[np.ndarray]:
+    """Sequence positions each device of a KV-parallel group stores, in its
+    local order, when the KV of new tokens is appended round-robin (Helix
+    article, KV cache section: the first block of new tokens goes to device
+    0, the next block to device 1, and so on).  The blocks are dealt in
+    sequence order; the last one may be short."""
+    shards: list[list[int]] = [[] for _ in range(P)]
+    dev = 0
+    for start in range(0, total, block):
+        shards[dev].extend(range(start, min(start + block, total)))
+        dev = (dev + 1) % P
+    return [np.asarray(x, dtype=np.int64) for x in shards]
+
+
 def unmasked_pairs(S: int, P: int, layout: str, rank: int, causal: bool = True) -> int:
     """Exact number of (query, key) pairs rank ``rank`` must score, counted by
     brute force over its query positions (global causal mask, section 4)."""

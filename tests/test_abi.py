@@ -16,6 +16,17 @@ FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
 NULL = ctypes.c_void_p(0)
 
 
+def _device_count() -> int:
+    import torch  # device_count() does not initialise the GPU runtime
+    return torch.cuda.device_count()
+
+
+# The rejection tests pass fake device pointers that only validation keeps
+# from a kernel.  Where a GPU is visible, a validation bug would turn them
+# into memory faults, so they run only where there is none.
+cpu_only = pytest.mark.skipif(_device_count() > 0, reason="fake-pointer tests run without a GPU")
+
+
 def declared_symbols():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
@@ -49,6 +60,7 @@ def _fwd_rank(**kw):
                                 a["dtype"], a["o_dtype"], NULL)
 
 
+@cpu_only
 @pytest.mark.parametrize("kw,code", [
     (dict(Q=NULL), ra.RA_ERR_INVALID_ARG),
     (dict(L=NULL), ra.RA_ERR_INVALID_ARG),
@@ -80,6 +92,7 @@ def test_fwd_rank_rejects(kw, code):
     assert ra.last_error() != ""
 
 
+@cpu_only
 def test_fwd_all_and_others_reject():
     L = ra.lib()
     assert L.ra_fwd_all(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 4, 4, 1000, 64, 3, 0, 0, 0, 0, NULL) \
@@ -122,6 +135,7 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
         ra.lib()
 
 
+@cpu_only
 def test_fwd_ws_rejects_before_the_device():
     L = ra.lib()
 
@@ -163,6 +177,7 @@ def test_fwd_workspace_bytes():
         f(1, 8, 8, 8192, 128, 8, False, True, "zigzag", 1, 65)
 
 
+@cpu_only
 def test_ring_step_rejects_before_the_device():
     L = ra.lib()
 
@@ -179,3 +194,42 @@ def test_ring_step_rejects_before_the_device():
     assert call(S=8200) == ra.RA_ERR_UNSUPPORTED
     assert call(d=80) == ra.RA_ERR_UNSUPPORTED
     assert call(Hq=6, Hkv=4) == ra.RA_ERR_UNSUPPORTED
+
+
+@cpu_only
+def test_round_robin_cache_rejects_before_the_device():
+    L = ra.lib()
+    # K_cache, V_cache, K_new, V_new, B, Hkv, d, P, cap, len, n_new, block, dtype
+    ok = dict(B=2, Hkv=8, d=128, P=4, cap=64, len=100, n=8, block=16, dt=1)
+
+    def app(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return L.ra_kv_append_rr(FAKE, FAKE, FAKE, FAKE, a["B"], a["Hkv"], a["d"], a["P"], a["cap"],
+                                 a["len"], a["n"], a["block"], a["dt"], NULL)
+
+    assert app(n=0) == ra.RA_ERR_INVALID_ARG
+    assert app(len=-1) == ra.RA_ERR_INVALID_ARG
+    assert app(block=0) == ra.RA_ERR_INVALID_ARG
+    assert app(dt=7) == ra.RA_ERR_INVALID_ARG
+    assert app(d=96) == ra.RA_ERR_UNSUPPORTED
+    # 108 keys in blocks of 16 over 4 shards: shard 0 holds blocks 0 and 4 (32 rows);
+    # 257 keys: blocks 0, 4, 8, 12, 16 (the last one key) -> 65 rows > 64
+    assert app(len=200, n=57) == ra.RA_ERR_INVALID_ARG
+    assert "capacity" in ra.last_error()
+    assert L.ra_kv_append_rr(ctypes.c_void_p(0x1008), FAKE, FAKE, FAKE, 2, 8, 128, 4, 64, 100, 8, 16,
+                             1, NULL) == ra.RA_ERR_INVALID_ARG   # misaligned
+    assert "aligned" in ra.last_error()
+
+    def dec(**kw):
+        a = dict(B=2, Hq=16, Hkv=8, Sq=1, cap=64, len=100, block=16, P=4, pps=2, d=128, dt=1)
+        a.update(kw)
+        return L.ra_attn_partial_rr(FAKE, FAKE, FAKE, FAKE, FAKE, a["B"], a["Hq"], a["Hkv"], a["Sq"],
+                                    a["cap"], a["len"], a["block"], a["P"], a["pps"], a["d"], a["dt"],
+                                    NULL)
+
+    assert dec(len=0) == ra.RA_ERR_INVALID_ARG
+    assert dec(pps=0) == ra.RA_ERR_INVALID_ARG
+    assert dec(len=257) == ra.RA_ERR_INVALID_ARG                   # shard 0 needs 65 rows
+    assert dec(Hq=12) == ra.RA_ERR_UNSUPPORTED
+    assert dec(Sq=5, Hq=64) == ra.RA_ERR_UNSUPPORTED               # 5 x 8 rows exceed 32

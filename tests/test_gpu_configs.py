@@ -136,3 +136,50 @@ def test_decode_workload():
         O_ref, L_ref = oracle.attention_rows(qh[b:b + 1], Kb, Vb, False, [0], [0])
         e = check(O_g[b][None], O_ref, L_g[b][None], L_ref, "bf16", f"sequence {b}")
         log(f"workload 5 sequence {b}: ok {fmt(e)}")
+
+
+def test_decode_workload_round_robin_cache():
+    """The 1M-key decode workload with its cache dealt round-robin in blocks
+    of 64 tokens over the 8 shards (built by ra_kv_append_rr), 8 parts per
+    shard, merged; checked against the oracle on two whole sequences."""
+    w = WORKLOADS[5]
+    block, pps = 64, 8
+    log(f"workload 5 {w.name}: round-robin cache, blocks of {block}")
+    Q = synthetic.to_device(w.q_shape, w.seed(0), "bf16")
+    shards = oracle.helix_round_robin(w.S, block, w.P)
+    cap = max(len(x) for x in shards)
+    Kc = torch.empty(w.P, w.B, cap, w.Hkv, w.d, dtype=torch.bfloat16, device="cuda")
+    Vc = torch.empty_like(Kc)
+    K = synthetic.to_device(w.kv_shape, w.seed(1), "bf16")
+    V = synthetic.to_device(w.kv_shape, w.seed(2), "bf16")
+    cut = 777_777  # two appends, the second starting inside a block
+    ra.ra_kv_append_rr(Kc, Vc, K[:, :cut].contiguous(), V[:, :cut].contiguous(), 0, block)
+    ra.ra_kv_append_rr(Kc, Vc, K[:, cut:].contiguous(), V[:, cut:].contiguous(), cut, block)
+    torch.cuda.synchronize()
+    del K, V
+    torch.cuda.empty_cache()
+    rows = w.B * w.Sq * w.Hq
+    parts = w.P * pps
+    Op = torch.empty(parts, rows, w.d, dtype=torch.float32, device="cuda")
+    lp = torch.empty(parts, rows, dtype=torch.float32, device="cuda")
+    O = torch.empty(rows, w.d, dtype=torch.float32, device="cuda")
+    lse = torch.empty(rows, dtype=torch.float32, device="cuda")
+    log("workload 5: ra_attn_partial_rr + ra_merge_partials")
+    ra.ra_attn_partial_rr(Q, Kc, Vc, Op, lp, w.S, block, pps)
+    ra.ra_merge_partials(Op, lp, O, lse)
+    torch.cuda.synchronize()
+    O_g = from_dev(O).reshape(w.B, w.Hq, w.d)
+    L_g = from_dev(lse).reshape(w.B, w.Hq)
+    qh = Q.cpu().view(torch.int16).numpy().view(np.uint16)
+    del Kc, Vc, Op, lp
+    torch.cuda.empty_cache()
+    per_seq = w.S * w.Hkv * w.d
+    for b in (0, w.B - 1):
+        log(f"workload 5 round-robin: oracle on sequence {b}")
+        Kb = synthetic.normal_range(w.seed(1), b * per_seq, (b + 1) * per_seq, "bf16")
+        Vb = synthetic.normal_range(w.seed(2), b * per_seq, (b + 1) * per_seq, "bf16")
+        Kb = Kb.reshape(1, w.S, w.Hkv, w.d)
+        Vb = Vb.reshape(1, w.S, w.Hkv, w.d)
+        O_ref, L_ref = oracle.attention_rows(qh[b:b + 1], Kb, Vb, False, [0], [0])
+        e = check(O_g[b][None], O_ref, L_g[b][None], L_ref, "bf16", f"round-robin sequence {b}")
+        log(f"workload 5 round-robin sequence {b}: ok {fmt(e)}")

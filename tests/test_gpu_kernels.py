@@ -436,3 +436,63 @@ def test_ring_step_double_buffered_streams():
         free[t % 2].record(comp)
     torch.cuda.synchronize()
     assert torch.equal(O, ref_O) and torch.equal(L, ref_L)
+
+
+RR = [  # B, Sq, Hq, Hkv, d, P, block, total, dtype, parts_per_shard
+    (2, 1, 16, 8, 128, 4, 16, 1000, "bf16", 2),
+    (1, 2, 8, 1, 64, 3, 7, 200, "bf16", 3),
+    (2, 1, 4, 2, 128, 8, 5, 37, "f32", 1),
+    (1, 1, 8, 8, 128, 8, 5, 20, "bf16", 2),      # shards 4..7 stay empty
+]
+
+
+@pytest.mark.parametrize("case", RR, ids=[str(c) for c in RR])
+def test_round_robin_cache_append_and_decode(case):
+    """Tokens appended in uneven pieces land where the dealing of blocks
+    puts them (bit-exact, other rows untouched); decoding over the P shard
+    caches and merging the partials gives attention over all keys."""
+    B, Sq, Hq, Hkv, d, P, block, total, dtype, pps = case
+    log(f"round-robin cache {case}")
+    Qn, Kn, Vn = qkv(B, Sq, total, Hq, Hkv, d, dtype, (1400, total, P))
+    shards = oracle.helix_round_robin(total, block, P)
+    cap = max(len(x) for x in shards) + 3
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    Kc = torch.empty(P, B, cap, Hkv, d, dtype=tdt, device="cuda")
+    Vc = torch.empty_like(Kc)
+    Kc.view(torch.uint8).fill_(0xAB)
+    Vc.view(torch.uint8).fill_(0xCD)
+    Kd, Vd = to_dev(Kn), to_dev(Vn)
+    rng = np.random.default_rng(1401)
+    pos = 0
+    while pos < total:
+        step = int(min(total - pos, rng.choice([1, 2, 5, 37, 130])))
+        ra.ra_kv_append_rr(Kc, Vc, Kd[:, pos:pos + step].contiguous(), Vd[:, pos:pos + step].contiguous(),
+                           pos, block)
+        pos += step
+    torch.cuda.synchronize()
+    Kh = Kc.cpu().view(torch.uint8).numpy()
+    Vh = Vc.cpu().view(torch.uint8).numpy()
+    Kb = Kd.cpu().view(torch.uint8).numpy()
+    Vb = Vd.cpu().view(torch.uint8).numpy()
+    for p_, idx in enumerate(shards):
+        L_ = len(idx)
+        assert np.array_equal(Kh[p_, :, :L_], Kb[:, idx]), f"K shard {p_}"
+        assert np.array_equal(Vh[p_, :, :L_], Vb[:, idx]), f"V shard {p_}"
+        assert np.all(Kh[p_, :, L_:] == 0xAB) and np.all(Vh[p_, :, L_:] == 0xCD), f"shard {p_} tail"
+    rows = B * Sq * Hq
+    Op = torch.empty(P * pps, rows, d, dtype=torch.float32, device="cuda")
+    lp = torch.empty(P * pps, rows, dtype=torch.float32, device="cuda")
+    O = torch.empty(rows, d, dtype=torch.float32, device="cuda")
+    lse = torch.empty(rows, dtype=torch.float32, device="cuda")
+    ra.ra_attn_partial_rr(to_dev(Qn), Kc, Vc, Op, lp, total, block, pps)
+    ra.ra_merge_partials(Op, lp, O, lse)
+    torch.cuda.synchronize()
+    O_ref, L_ref = oracle.attention(Qn, Kn, Vn, False)
+    O_g = from_dev(O).reshape(B, Sq, Hq, d)
+    L_g = from_dev(lse).reshape(B, Sq, Hq).transpose(0, 2, 1)
+    e = check(O_g, O_ref, L_g, L_ref, dtype, str(case))
+    log(f"  ok {fmt(e)}")
+    # partials of empty shards carry no weight
+    for p_, idx in enumerate(shards):
+        if len(idx) == 0:
+            assert torch.all(torch.isneginf(lp[p_ * pps:(p_ + 1) * pps]))

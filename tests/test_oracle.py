@@ -518,3 +518,52 @@ def test_planted_layout_mistakes_fail_a_pin():
     n = S // P
     contiguous_as_striped = [sum(range(r * n + 1, (r + 1) * n + 1)) for r in range(P)]
     assert contiguous_as_striped != [n * (r + 1) + P * n * (n - 1) // 2 for r in range(P)]
+
+
+# ------------------------------------------------------ round-robin KV cache
+
+def test_helix_round_robin_hand_written():
+    # 10 tokens in blocks of 2 over 3 devices: blocks 0..4 go to devices
+    # 0, 1, 2, 0, 1 (written out by hand)
+    got = [x.tolist() for x in oracle.helix_round_robin(10, 2, 3)]
+    assert got == [[0, 1, 6, 7], [2, 3, 8, 9], [4, 5]]
+    # a short last block
+    got = [x.tolist() for x in oracle.helix_round_robin(7, 3, 2)]
+    assert got == [[0, 1, 2, 6], [3, 4, 5]]
+    assert [x.tolist() for x in oracle.helix_round_robin(0, 4, 2)] == [[], []]
+
+
+@pytest.mark.parametrize("total,block,P", [(1, 1, 1), (100, 16, 8), (1000, 7, 3), (4096, 64, 8),
+                                           (33, 40, 4)])
+def test_helix_round_robin_balance(total, block, P):
+    sh = oracle.helix_round_robin(total, block, P)
+    allpos = np.concatenate(sh)
+    assert sorted(allpos.tolist()) == list(range(total))     # every token exactly once
+    lens = [len(x) for x in sh]
+    assert max(lens) - min(lens) <= block                    # memory grows evenly
+    assert lens[0] == max(lens)                              # device 0 is served first
+    for x in sh:
+        assert np.all(np.diff(x) > 0)                        # local order is sequence order
+    # appending one token at a time deals the same positions
+    inc = [[] for _ in range(P)]
+    for t in range(total):
+        inc[(t // block) % P].append(t)
+    assert [x.tolist() for x in sh] == inc
+
+
+def test_decode_over_round_robin_shards_equals_full():
+    # the merge of per-device partials over the round-robin shards is the
+    # attention over all keys, whatever the dealing
+    B, Skv, Hq, Hkv, d = 2, 57, 4, 2, 8
+    Q = _rand((B, 1, Hq, d), (50,))
+    K = _rand((B, Skv, Hkv, d), (51,))
+    V = _rand((B, Skv, Hkv, d), (52,))
+    O, lse = oracle.attention(Q, K, V, False)
+    parts_O, parts_l = [], []
+    for pos in oracle.helix_round_robin(Skv, 5, 4):
+        Op, lp = oracle.attention(Q, K[:, pos], V[:, pos], False)
+        parts_O.append(Op.reshape(B * Hq, d))
+        parts_l.append(lp.reshape(B * Hq))
+    Om, lm = oracle.merge(np.stack(parts_O), np.stack(parts_l))
+    np.testing.assert_allclose(Om, O.reshape(B * Hq, d), atol=1e-12)
+    np.testing.assert_allclose(lm, lse.reshape(B * Hq), atol=1e-12)
