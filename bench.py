@@ -21,7 +21,8 @@ of the same prefill workload.
 
 --layout runs the same prefill shape under another split (contiguous,
 striped, zigzag<k>); --prefill-cfg picks the 32k or 8k-token workload
-instead; --ring-steps times the rank share as P separate ring steps with
+instead; --ulysses times the whole problem as the Ulysses all-to-all scheme
+beside the ring; --ring-steps times the rank share as P separate ring steps with
 the state in HBM (blocks resident, and double-buffered copies on a second
 stream standing in for the peer-to-peer receive); --all-ranks adds the time of every rank's share, whose maximum is
 the length of one ring pass when the ranks run side by side, and of all
@@ -122,6 +123,10 @@ def main() -> int:
                     help="decode over the KV cache dealt round-robin in blocks of this many tokens "
                          "to the 8 shard caches (built by ra_kv_append_rr before timing); 0 = one "
                          "contiguous cache per sequence (default)")
+    ap.add_argument("--ulysses", action="store_true",
+                    help="also time the whole prefill problem as DeepSpeed Ulysses on one GPU: "
+                         "all-to-all of Q, K, V to head groups, full-sequence attention of all "
+                         "groups, all-to-all of O and LSE back; beside the ring (ra_fwd_all_ws)")
     ap.add_argument("--ring-steps", action="store_true",
                     help="also time the timed rank's share as P ring steps (ra_ring_step) on one "
                          "stream, and double-buffered with the next block copied on a second stream")
@@ -425,6 +430,79 @@ def main() -> int:
                              "fused_ms": ms["prefill"], "block_bytes_per_step": blk_bytes,
                              "overhead_vs_fused": t_db / ms["prefill"] - 1.0}
         del O_s, L_s, bufK, bufV
+    if do_pre and args.ulysses:
+        P_, B_, S_ = wp.P, wp.B, wp.S
+        if wp.Hq % P_ or wp.Hkv % P_:
+            raise SystemExit("Ulysses needs the heads to divide by the ranks")
+        log("timing the Ulysses all-to-all scheme and the ring on the whole problem")
+        Qh = torch.empty(P_ * B_, S_, wp.Hq // P_, wp.d, dtype=torch.bfloat16, device=dev)
+        Kh = torch.empty(P_ * B_, S_, wp.Hkv // P_, wp.d, dtype=torch.bfloat16, device=dev)
+        Vh = torch.empty_like(Kh)
+        Oh = torch.empty(P_ * B_, S_, wp.Hq // P_, wp.d, dtype=torch.float32, device=dev)
+        Lh = torch.empty(P_ * B_, wp.Hq // P_, S_, dtype=torch.float32, device=dev)
+        O_n = torch.empty(B_, S_, wp.Hq, wp.d, dtype=torch.float32, device=dev)
+        L_n = torch.empty(B_, wp.Hq, S_, dtype=torch.float32, device=dev)
+        wsu_bytes = ra.ra_fwd_workspace_bytes(P_ * B_, wp.Hq // P_, wp.Hkv // P_, S_, wp.d, 1, True,
+                                              wp.causal, "contiguous", ra.DTYPE_BF16, 0)
+        wsu = torch.empty(max(wsu_bytes, 1), dtype=torch.uint8, device=dev)
+        qrun, kvrun = wp.Hq // P_ * wp.d * 2, wp.Hkv // P_ * wp.d * 2
+
+        def u_in():
+            ra.ra_head_a2a(Qn, Qh, B_, S_, P_, qrun, False)
+            ra.ra_head_a2a(Kn, Kh, B_, S_, P_, kvrun, False)
+            ra.ra_head_a2a(Vn, Vh, B_, S_, P_, kvrun, False)
+
+        def u_attn():
+            ra.ra_fwd_all_ws(Qh, Kh, Vh, Oh, Lh, 1, wp.causal, "contiguous", 0, wsu)
+
+        def u_out():
+            ra.ra_head_a2a(Oh, O_n, B_, S_, P_, wp.Hq // P_ * wp.d * 4, True)
+            ra.ra_head_a2a(Lh, L_n, B_, 1, P_, wp.Hq // P_ * S_ * 4, True)
+
+        O_all = torch.empty(B_, S_, wp.Hq, wp.d, dtype=torch.float32, device=dev)
+        L_all = torch.empty(B_, wp.Hq, S_, dtype=torch.float32, device=dev)
+        wsr_bytes = ra.ra_fwd_workspace_bytes(B_, wp.Hq, wp.Hkv, S_, wp.d, P_, True, wp.causal,
+                                              wp.layout, ra.DTYPE_BF16, 0)
+        wsr = torch.empty(max(wsr_bytes, 1), dtype=torch.uint8, device=dev)
+
+        def ring_all():
+            ra.ra_fwd_all_ws(Qs, Ks, Vs, O_all, L_all, P_, wp.causal, wp.layout, 0, wsr)
+
+        def tfn(fn, k):
+            for _ in range(args.warmup):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(k):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / k
+
+        k_ = max(1, min(args.steps, 3))
+        t_in, t_attn, t_out = tfn(u_in, k_), tfn(u_attn, k_), tfn(u_out, k_)
+        t_ring = tfn(ring_all, k_)
+        total = prefill_flops(wp)
+        n_ = S_ // P_
+        eb = 2
+        # per rank during attention: ring = Q_r, own K/V shard, one received K/V
+        # block, fp32 O_r; Ulysses = the rank's sequence shard of Q/K/V (the
+        # all-to-all's send side), its head group of Q/K/V for the whole
+        # sequence, fp32 O of that head group
+        ring_mem = (n_ * wp.Hq * wp.d * eb + 2 * (2 * n_ * wp.Hkv * wp.d * eb)
+                    + n_ * wp.Hq * wp.d * 4) * B_
+        uly_mem = (n_ * (wp.Hq + 2 * wp.Hkv) * wp.d * eb + S_ * (wp.Hq + 2 * wp.Hkv) // P_ * wp.d * eb
+                   + S_ * wp.Hq // P_ * wp.d * 4) * B_
+        out["ulysses"] = {
+            "a2a_in_ms": t_in, "attention_ms": t_attn, "a2a_out_ms": t_out,
+            "total_ms": t_in + t_attn + t_out, "ring_fwd_all_ms": t_ring,
+            "tflops_ulysses": total / ((t_in + t_attn + t_out) * 1e-3) / 1e12,
+            "tflops_ring": total / (t_ring * 1e-3) / 1e12,
+            "per_rank_bytes_ring": ring_mem, "per_rank_bytes_ulysses": uly_mem,
+            "note": "one GPU: the all-to-all is a local transposition; the ring's block exchange is "
+                    "not simulated (all shards resident)"}
+        del Qh, Kh, Vh, Oh, Lh, O_n, L_n, O_all, L_all, wsu, wsr
     if do_pre and not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on {args.cpu_rows} sampled rows")
         out["cpu_baseline"] = cpu_baseline(wp, args.rank, args.cpu_rows)

@@ -281,6 +281,23 @@ int ra_attn_partial_rr(const void* Q, const void* K_cache, const void* V_cache, 
 int ra_layout_gather(const void* src, void* dst, int64_t outer, int64_t S,
                      int64_t inner_bytes, int P, int layout, int inverse, void* stream);
 
+/*
+ * ra_head_a2a -- the all-to-all of DeepSpeed Ulysses ([L8] section 5): the
+ * sequence-sharded tensors are transposed so that rank g holds head group g
+ * (H/P heads) of every token; attention then runs per rank over the whole
+ * sequence, and the same exchange brings the output back.  On one GPU the
+ * P ranks' buffers are one tensor, so the exchange is a transposition:
+ *   inverse = 0: src [B, S, P, run] -> dst [P, B, S, run]
+ *   inverse = 1: src [P, B, S, run] -> dst [B, S, P, run]
+ * where run = run_bytes is one head group of one token (H/P * d * elem for
+ * Q/K/V/O).  For an LSE stored [P, B, H/P, S] use S = 1 and run =
+ * H/P * S * 4 to reach [B, H, S].  The heads must divide by P (the caller
+ * forms run_bytes).  run_bytes a multiple of 16, pointers 16-byte aligned,
+ * src and dst must not overlap.
+ */
+int ra_head_a2a(const void* src, void* dst, int64_t B, int64_t S, int P, int64_t run_bytes,
+                int inverse, void* stream);
+
 /* Message describing the calling thread's last non-OK status ("" if none). */
 const char* ra_last_error(void);
 

@@ -28,7 +28,7 @@ def layout_zigzag_k(k: int) -> int:
 DTYPE_F32, DTYPE_BF16 = 0, 1
 
 EXPORTS = ("ra_fwd_rank", "ra_fwd_all", "ra_fwd_rank_ws", "ra_fwd_all_ws", "ra_fwd_workspace_bytes",
-           "ra_ring_step", "ra_kv_append_rr", "ra_attn_partial_rr",
+           "ra_ring_step", "ra_kv_append_rr", "ra_attn_partial_rr", "ra_head_a2a",
            "ra_merge_partials", "ra_attn_partial",
            "ra_layout_gather", "ra_last_error", "ra_version")
 
@@ -61,6 +61,7 @@ def lib() -> ctypes.CDLL:
         L.ra_fwd_workspace_bytes.argtypes = [i32, i32, i32, i64, i32, i32, i32, i32, i32, i32, i32]
         L.ra_ring_step.argtypes = [vp, vp, vp, fp, fp, i32, i32, i32, i64, i32, i32, i32, i32, i32,
                                    i32, i32, vp]
+        L.ra_head_a2a.argtypes = [vp, vp, i64, i64, i32, i64, i32, vp]
         L.ra_kv_append_rr.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i64, i64, i64, i64, i32, vp]
         L.ra_attn_partial_rr.argtypes = [vp, vp, vp, fp, fp, i32, i32, i32, i64, i64, i64, i64, i32,
                                          i32, i32, i32, vp]
@@ -69,7 +70,7 @@ def lib() -> ctypes.CDLL:
         L.ra_attn_partial.argtypes = [vp, vp, vp, fp, fp, i32, i32, i32, i64, i64, i32, i32, i32, vp]
         L.ra_layout_gather.argtypes = [vp, vp, i64, i64, i64, i32, i32, i32, vp]
         for f in ("ra_fwd_rank", "ra_fwd_all", "ra_fwd_rank_ws", "ra_fwd_all_ws", "ra_ring_step",
-                  "ra_kv_append_rr", "ra_attn_partial_rr",
+                  "ra_kv_append_rr", "ra_attn_partial_rr", "ra_head_a2a",
                   "ra_merge_partials", "ra_attn_partial", "ra_layout_gather"):
             getattr(L, f).restype = ctypes.c_int
         L.ra_last_error.restype = ctypes.c_char_p
@@ -280,6 +281,17 @@ def ra_attn_partial_rr(Q, K_cache, V_cache, O_parts, lse_parts, length: int, blo
                                     _dev(O_parts, "O_parts"), _dev(lse_parts, "lse_parts"), B, Hq,
                                     Hkv, Sq, cap, int(length), int(block), P, int(parts_per_shard),
                                     d, _dtype_code(Q), _stream(stream)))
+
+
+def ra_head_a2a(src, dst, B: int, S: int, P: int, run_bytes: int, inverse: bool, stream=None):
+    """Ulysses all-to-all: src [B, S, P, run] -> dst [P, B, S, run] (inverse:
+    back), run = one head group of one token in bytes."""
+    nbytes = int(B) * int(S) * int(P) * int(run_bytes)
+    for t, name in ((src, "src"), (dst, "dst")):
+        if t.numel() * t.element_size() != nbytes:
+            raise ValueError(f"{name} must hold B*S*P*run_bytes bytes")
+    _check(lib().ra_head_a2a(_dev(src, "src"), _dev(dst, "dst"), int(B), int(S), int(P),
+                             int(run_bytes), int(bool(inverse)), _stream(stream)))
 
 
 def ra_merge_partials(O_parts, lse_parts, O, lse=None, stream=None):

@@ -449,6 +449,24 @@ int ra_layout_gather(const void* src, void* dst, int64_t outer, int64_t S, int64
                       "layout kernel launch");
 }
 
+int ra_head_a2a(const void* src, void* dst, int64_t B, int64_t S, int P, int64_t run_bytes,
+                int inverse, void* stream) {
+    if (!src || !dst) return fail(RA_ERR_INVALID_ARG, "null tensor pointer");
+    if (B <= 0 || S <= 0 || P <= 0 || run_bytes <= 0) return fail(RA_ERR_INVALID_ARG, "sizes must be positive");
+    if (inverse != 0 && inverse != 1) return fail(RA_ERR_INVALID_ARG, "inverse must be 0 or 1");
+    if (run_bytes % 16 != 0 || ((uintptr_t)src | (uintptr_t)dst) % 16 != 0)
+        return fail(RA_ERR_UNSUPPORTED, "runs of %lld bytes: need 16-byte runs and alignment",
+                    (long long)run_bytes);
+    const int64_t runs = (int64_t)P * B * S;
+    if ((runs + 3) / 4 > 0x7fffffffLL) return fail(RA_ERR_UNSUPPORTED, "too many runs");
+    const uint8_t* s0 = (const uint8_t*)src;
+    const uint8_t* d0 = (const uint8_t*)dst;
+    const int64_t bytes = runs * run_bytes;
+    if (s0 < d0 + bytes && d0 < s0 + bytes) return fail(RA_ERR_INVALID_ARG, "src and dst overlap");
+    return hip_status(ra::launch_head_a2a(src, dst, B, S, P, run_bytes, inverse, (hipStream_t)stream),
+                      "all-to-all kernel launch");
+}
+
 const char* ra_last_error(void) { return g_err; }
 
 const char* ra_version(void) { return "libra 0.1 (gfx950)"; }

@@ -123,7 +123,55 @@ __global__ __launch_bounds__(256) void layout_rows_kernel(RowArgs a) {
     }
 }
 
+// Head all-to-all of the Ulysses scheme (lesson 8, section 5): every rank
+// sends head group g of its sequence shard to rank g.  With the token's heads
+// cut into P runs of run_bytes (H/P heads each), forward moves
+// [B, S, P, run] (sequence order, all heads) to [P, B, S, run] (head group
+// major: each group holds every token), inverse moves it back.  One wave per
+// destination run, enumerated in destination order, 16 bytes per lane.
+struct A2AArgs {
+    const uint8_t* src;
+    uint8_t* dst;
+    int64_t B, S, runs, run_bytes;  // runs = P * B * S
+    int P, inverse;
+};
+
+__global__ __launch_bounds__(256) void head_a2a_kernel(A2AArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int64_t k = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // destination run
+    if (k >= a.runs) return;
+    int64_t srun;
+    if (!a.inverse) {  // k = (g * B + b) * S + x  <-  (b * S + x) * P + g
+        const int64_t g = k / (a.B * a.S), bx = k - g * a.B * a.S;
+        srun = bx * a.P + g;
+    } else {           // k = (b * S + x) * P + g  <-  (g * B + b) * S + x
+        const int64_t bx = k / a.P, g = k - bx * a.P;
+        srun = g * a.B * a.S + bx;
+    }
+    const uint4* s = (const uint4*)(a.src + srun * a.run_bytes);
+    uint4* d = (uint4*)(a.dst + k * a.run_bytes);
+    const int units = (int)(a.run_bytes >> 4);
+    for (int u = lane; u < units; u += 64) d[u] = load_once16(s + u);
+}
+
 }  // namespace
+
+hipError_t launch_head_a2a(const void* src, void* dst, int64_t B, int64_t S, int P, int64_t run_bytes,
+                           int inverse, hipStream_t s) {
+    A2AArgs a;
+    a.src = (const uint8_t*)src;
+    a.dst = (uint8_t*)dst;
+    a.B = B;
+    a.S = S;
+    a.P = P;
+    a.runs = (int64_t)P * B * S;
+    a.run_bytes = run_bytes;
+    a.inverse = inverse;
+    const int64_t grid = (a.runs + 3) / 4;
+    if (grid <= 0) return hipSuccess;
+    hipLaunchKernelGGL(head_a2a_kernel, dim3((unsigned)grid), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
 
 hipError_t launch_layout(const void* src, void* dst, int64_t outer, int64_t S, int64_t inner_bytes,
                          int P, int chunks_per_rank, int striped, int inverse, hipStream_t s) {

@@ -106,6 +106,8 @@ hipError_t launch_merge(const MergeParams& p, int d, hipStream_t s);
 hipError_t launch_kv_append_rr(void* K_cache, void* V_cache, const void* K_new, const void* V_new,
                               int B, int64_t row_bytes, int P, int64_t cap, int64_t len,
                               int64_t n_new, int64_t block, hipStream_t s);
+hipError_t launch_head_a2a(const void* src, void* dst, int64_t B, int64_t S, int P, int64_t run_bytes,
+                           int inverse, hipStream_t s);
 hipError_t launch_layout(const void* src, void* dst, int64_t outer, int64_t S, int64_t inner_bytes,
                          int P, int chunks_per_rank, int striped, int inverse, hipStream_t s);
 

@@ -148,6 +148,26 @@ def natural_positions(S: int, P: int, layout: str) -> np.ndarray:
     return np.concatenate(pos)
 
 
+def ulysses_scatter_heads(x: np.ndarray, P: int) -> np.ndarray:
+    """The all-to-all of DeepSpeed Ulysses (lesson 8, section 5): [B, S, H, ...]
+    in sequence order -> [P, B, S, H/P, ...], rank g holding head group g
+    (heads g*H/P .. (g+1)*H/P - 1) of every token.  The heads must divide by
+    the number of ranks."""
+    B, S, H = x.shape[:3]
+    if H % P:
+        raise ValueError(f"{H} heads do not divide over {P} ranks")
+    out = np.empty((P, B, S, H // P) + x.shape[3:], dtype=x.dtype)
+    for g in range(P):
+        out[g] = x[:, :, g * (H // P):(g + 1) * (H // P)]
+    return out
+
+
+def ulysses_gather_heads(y: np.ndarray) -> np.ndarray:
+    """Inverse of ``ulysses_scatter_heads``: [P, B, S, H/P, ...] -> [B, S, H, ...]."""
+    P = y.shape[0]
+    return np.concatenate([y[g] for g in range(P)], axis=2)
+
+
 def helix_round_robin(total: int, block: int, P: int) -> list[np.ndarray]:
     """Sequence positions each device of a KV-parallel group stores, in its
     local order, when the KV of new tokens is appended round-robin (Helix

@@ -30,7 +30,7 @@ cpu_only = pytest.mark.skipif(_device_count() > 0, reason="fake-pointer tests ru
 def declared_symbols():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(ra_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(ra_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_binding_names():
@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(L, name), name
     out = subprocess.run(["nm", "-D", "--defined-only", ra.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
-    exported = set(re.findall(r" T (ra_[a-z_]+)$", out, flags=re.M))
+    exported = set(re.findall(r" T (ra_[a-z0-9_]+)$", out, flags=re.M))
     assert set(declared_symbols()) <= exported
 
 
@@ -233,3 +233,13 @@ def test_round_robin_cache_rejects_before_the_device():
     assert dec(len=257) == ra.RA_ERR_INVALID_ARG                   # shard 0 needs 65 rows
     assert dec(Hq=12) == ra.RA_ERR_UNSUPPORTED
     assert dec(Sq=5, Hq=64) == ra.RA_ERR_UNSUPPORTED               # 5 x 8 rows exceed 32
+
+
+@cpu_only
+def test_head_a2a_rejects_before_the_device():
+    L = ra.lib()
+    assert L.ra_head_a2a(FAKE, FAKE, 1, 8, 2, 0, 0, NULL) == ra.RA_ERR_INVALID_ARG
+    assert L.ra_head_a2a(FAKE, FAKE, 1, 8, 2, 64, 2, NULL) == ra.RA_ERR_INVALID_ARG
+    assert L.ra_head_a2a(FAKE, FAKE, 1, 8, 2, 24, 0, NULL) == ra.RA_ERR_UNSUPPORTED   # 24-byte runs
+    assert L.ra_head_a2a(FAKE, FAKE, 1, 8, 2, 64, 0, NULL) == ra.RA_ERR_INVALID_ARG   # overlap
+    assert L.ra_head_a2a(NULL, FAKE, 1, 8, 2, 64, 0, NULL) == ra.RA_ERR_INVALID_ARG

@@ -496,3 +496,56 @@ def test_round_robin_cache_append_and_decode(case):
     for p_, idx in enumerate(shards):
         if len(idx) == 0:
             assert torch.all(torch.isneginf(lp[p_ * pps:(p_ + 1) * pps]))
+
+
+@pytest.mark.parametrize("inverse", [False, True])
+@pytest.mark.parametrize("B,S,P,run", [(2, 37, 4, 256), (1, 100, 8, 1024), (3, 5, 2, 16), (1, 9, 3, 2064)])
+def test_head_a2a_bit_exact(B, S, P, run, inverse):
+    rng = np.random.default_rng([1600, B, S, P, run])
+    if not inverse:
+        x = rng.integers(0, 256, size=(B, S, P, run), dtype=np.uint8)
+        expect = np.ascontiguousarray(x.transpose(2, 0, 1, 3))
+    else:
+        x = rng.integers(0, 256, size=(P, B, S, run), dtype=np.uint8)
+        expect = np.ascontiguousarray(x.transpose(1, 2, 0, 3))
+    src = torch.from_numpy(x).cuda()
+    dst = torch.empty(expect.shape, dtype=torch.uint8, device="cuda")
+    ra.ra_head_a2a(src, dst, B, S, P, run, inverse)
+    torch.cuda.synchronize()
+    assert np.array_equal(dst.cpu().numpy(), expect)
+
+
+ULYSSES = [  # B, S, Hq, Hkv, d, P, causal, dtype
+    (1, 1024, 8, 2, 128, 2, True, "bf16"),
+    (2, 640, 8, 8, 64, 4, True, "bf16"),
+    (1, 520, 4, 4, 64, 4, False, "f32"),
+]
+
+
+@pytest.mark.parametrize("case", ULYSSES, ids=[str(c) for c in ULYSSES])
+def test_ulysses_pipeline(case):
+    """All-to-all of Q, K, V to head groups, full-sequence attention of every
+    group in one launch (the P groups as a batch, one shard), all-to-all of O
+    and LSE back: equals the oracle's attention."""
+    B, S, Hq, Hkv, d, P, causal, dtype = case
+    log(f"ulysses {case}")
+    Qn, Kn, Vn = qkv(B, S, S, Hq, Hkv, d, dtype, (1601, S, P))
+    es = 2 if dtype == "bf16" else 4
+    Qd, Kd, Vd = to_dev(Qn), to_dev(Kn), to_dev(Vn)
+    Qh = torch.empty(P * B, S, Hq // P, d, dtype=Qd.dtype, device="cuda")
+    Kh = torch.empty(P * B, S, Hkv // P, d, dtype=Kd.dtype, device="cuda")
+    Vh = torch.empty_like(Kh)
+    ra.ra_head_a2a(Qd, Qh, B, S, P, Hq // P * d * es, False)
+    ra.ra_head_a2a(Kd, Kh, B, S, P, Hkv // P * d * es, False)
+    ra.ra_head_a2a(Vd, Vh, B, S, P, Hkv // P * d * es, False)
+    Oh = torch.empty(P * B, S, Hq // P, d, dtype=torch.float32, device="cuda")
+    Lh = torch.empty(P * B, Hq // P, S, dtype=torch.float32, device="cuda")
+    ra.ra_fwd_all(Qh, Kh, Vh, Oh, Lh, 1, causal, "contiguous")
+    O = torch.empty(B, S, Hq, d, dtype=torch.float32, device="cuda")
+    L = torch.empty(B, Hq, S, dtype=torch.float32, device="cuda")
+    ra.ra_head_a2a(Oh, O, B, S, P, Hq // P * d * 4, True)
+    ra.ra_head_a2a(Lh, L, B, 1, P, Hq // P * S * 4, True)
+    torch.cuda.synchronize()
+    O_ref, lse_ref = oracle.attention(Qn, Kn, Vn, causal)
+    e = check(from_dev(O), O_ref, from_dev(L), lse_ref, dtype, str(case))
+    log(f"  ok {fmt(e)}")

@@ -567,3 +567,40 @@ def test_decode_over_round_robin_shards_equals_full():
     Om, lm = oracle.merge(np.stack(parts_O), np.stack(parts_l))
     np.testing.assert_allclose(Om, O.reshape(B * Hq, d), atol=1e-12)
     np.testing.assert_allclose(lm, lse.reshape(B * Hq), atol=1e-12)
+
+
+# ----------------------------------------------------------- Ulysses heads
+
+def test_ulysses_scatter_hand_written():
+    # B1, S2, H4 (d = 1) over 2 ranks: rank 0 gets heads 0, 1 of both tokens,
+    # rank 1 heads 2, 3 (written out by hand)
+    x = np.array([[[[0], [1], [2], [3]], [[10], [11], [12], [13]]]])
+    y = oracle.ulysses_scatter_heads(x, 2)
+    assert y[..., 0].tolist() == [[[[0, 1], [10, 11]]], [[[2, 3], [12, 13]]]]
+    assert np.array_equal(oracle.ulysses_gather_heads(y), x)
+    with pytest.raises(ValueError):
+        oracle.ulysses_scatter_heads(x, 3)       # heads must divide by the ranks
+
+
+def test_ulysses_memory_equals_ring():
+    # section 5: per rank the attention phase holds s * h / N, the ring's (s / N) * h
+    B, S, H, d, P = 1, 64, 8, 4, 4
+    x = np.zeros((B, S, H, d))
+    y = oracle.ulysses_scatter_heads(x, P)
+    assert y[0].size == oracle.natural_positions(S, P, "contiguous")[: S // P].size * H * d
+
+
+@pytest.mark.parametrize("Hq,Hkv,P", [(4, 4, 2), (8, 2, 2), (16, 4, 4)])
+def test_ulysses_attention_equals_full(Hq, Hkv, P):
+    # attention per head group over the whole sequence, gathered back, is full
+    # causal attention (GQA groups stay together since P divides Hkv)
+    B, S, d = 1, 24, 8
+    Q = _rand((B, S, Hq, d), (60, Hq))
+    K = _rand((B, S, Hkv, d), (61, Hkv))
+    V = _rand((B, S, Hkv, d), (62, Hkv))
+    O_t, lse_t = _sdpa_f64(Q, K, V, True)
+    Qg, Kg, Vg = (oracle.ulysses_scatter_heads(x, P) for x in (Q, K, V))
+    Og = np.stack([oracle.attention(Qg[g], Kg[g], Vg[g], True)[0] for g in range(P)])
+    Lg = np.stack([oracle.attention(Qg[g], Kg[g], Vg[g], True)[1] for g in range(P)])
+    np.testing.assert_allclose(oracle.ulysses_gather_heads(Og), O_t, atol=1e-12)
+    np.testing.assert_allclose(np.concatenate(list(Lg), axis=1), lse_t, atol=1e-12)
