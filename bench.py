@@ -98,8 +98,16 @@ def cpu_baseline(w, rank: int, n_rows: int):
     t0 = time.perf_counter()
     oracle.attention_rows(Q, K, V, True, np.zeros_like(rows), rows)
     dt = time.perf_counter() - t0
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": model,
             "sample": f"{len(rows)} query rows of rank {rank} evenly spaced over its {w.layout} "
                       f"rows, all {w.Hq} heads, {flops / 1e9:.1f} GFLOP, {dt:.1f} s wall"}
 

@@ -243,3 +243,14 @@ def test_head_a2a_rejects_before_the_device():
     assert L.ra_head_a2a(FAKE, FAKE, 1, 8, 2, 24, 0, NULL) == ra.RA_ERR_UNSUPPORTED   # 24-byte runs
     assert L.ra_head_a2a(FAKE, FAKE, 1, 8, 2, 64, 0, NULL) == ra.RA_ERR_INVALID_ARG   # overlap
     assert L.ra_head_a2a(NULL, FAKE, 1, 8, 2, 64, 0, NULL) == ra.RA_ERR_INVALID_ARG
+
+
+@cpu_only
+def test_valid_call_without_a_device_reports_hip_error():
+    # arguments pass validation, so the call reaches the runtime, which has no
+    # device here: a negative status and a message, no crash
+    L = ra.lib()
+    rc = L.ra_fwd_rank(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 8, 8192, 128, 8, 0, 1, 1, 1, 0, NULL)
+    assert rc == ra.RA_ERR_HIP
+    assert "launch" in ra.last_error()
+    assert L.ra_merge_partials(FAKE, FAKE, FAKE, NULL, 2, 10, 128, 1, NULL) == ra.RA_ERR_HIP

@@ -549,3 +549,35 @@ def test_ulysses_pipeline(case):
     O_ref, lse_ref = oracle.attention(Qn, Kn, Vn, causal)
     e = check(from_dev(O), O_ref, from_dev(L), lse_ref, dtype, str(case))
     log(f"  ok {fmt(e)}")
+
+
+def test_ring_step_state_checkpoint_resume():
+    """The running (O, LSE) state is the whole carried state of the ring:
+    saved to the host after step 3 and restored into fresh tensors, the
+    remaining steps finish bit-identical to an uninterrupted run."""
+    B, S, Hq, Hkv, d, P, layout = 1, 2048, 8, 2, 128, 8, "zigzag"
+    Qn, Kn, Vn = qkv(B, S, S, Hq, Hkv, d, "bf16", (1302,))
+    (Qs, Ks, Vs), _, _ = _run_prefill(Qn, Kn, Vn, P, layout, True, "bf16")
+    n = S // P
+    r = 5
+    ref_O, ref_L = _ring_rank(Qs, Ks, Vs, S, P, r, True, layout)
+    Qr = Qs[:, r * n:(r + 1) * n].contiguous()
+    O = torch.empty(B, n, Hq, d, dtype=torch.float32, device="cuda")
+    L = torch.empty(B, Hq, n, dtype=torch.float32, device="cuda")
+
+    def step(t, O_, L_):
+        s = (r - t) % P
+        ra.ra_ring_step(Qr, Ks[:, s * n:(s + 1) * n].contiguous(), Vs[:, s * n:(s + 1) * n].contiguous(),
+                        O_, L_, S, P, r, t, True, layout)
+
+    for t in range(4):
+        step(t, O, L)
+    torch.cuda.synchronize()
+    saved = (O.cpu().numpy().copy(), L.cpu().numpy().copy())
+    del O, L
+    O2 = torch.from_numpy(saved[0]).cuda()
+    L2 = torch.from_numpy(saved[1]).cuda()
+    for t in range(4, P):
+        step(t, O2, L2)
+    torch.cuda.synchronize()
+    assert torch.equal(O2, ref_O) and torch.equal(L2, ref_L)
