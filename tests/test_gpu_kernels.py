@@ -581,3 +581,55 @@ def test_ring_step_state_checkpoint_resume():
         step(t, O2, L2)
     torch.cuda.synchronize()
     assert torch.equal(O2, ref_O) and torch.equal(L2, ref_L)
+
+
+def _random_cases(n, seed):
+    """Seeded random prefill shapes: every split, mask, dtype and head dim,
+    GQA ratios 1-8, 1-8 ranks, ragged chunks; small enough for the oracle."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        P = int(rng.integers(1, 9))
+        layout = str(rng.choice(["contiguous", "zigzag", "zigzag3", "zigzag4", "striped"]))
+        k = {"contiguous": 1, "zigzag": 2, "zigzag3": 3, "zigzag4": 4, "striped": 1}[layout]
+        c = int(rng.integers(1, 200))            # tokens per chunk (ragged against the tiles)
+        S = c * k * P
+        if S > 3000:
+            continue
+        Hkv = int(rng.choice([1, 2, 4]))
+        G = int(rng.choice([1, 2, 4, 8]))
+        d = int(rng.choice([64, 128]))
+        B = int(rng.integers(1, 3))
+        dtype = str(rng.choice(["bf16", "bf16", "f32"]))
+        causal = bool(rng.integers(0, 2))
+        cases.append((B, S, Hkv * G, Hkv, d, P, layout, causal, dtype))
+    return cases
+
+
+RANDOM = _random_cases(24, 1700)
+
+
+@pytest.mark.parametrize("case", RANDOM, ids=[_id(c) for c in RANDOM])
+def test_prefill_random_shapes(case):
+    """Fused launch, a key-range split launch and the ring-step path of one
+    rank, each against the oracle."""
+    B, S, Hq, Hkv, d, P, layout, causal, dtype = case
+    log(f"random {_id(case)}")
+    Qn, Kn, Vn = qkv(B, S, S, Hq, Hkv, d, dtype, (1701, S, P, Hq, d))
+    (Qs, Ks, Vs), O, L = _run_prefill(Qn, Kn, Vn, P, layout, causal, dtype)
+    O_ref, lse_ref = oracle.attention(Qn, Kn, Vn, causal)
+    check(unshard(from_dev(O), S, P, layout, axis=1), O_ref, unshard(from_dev(L), S, P, layout, axis=2),
+          lse_ref, dtype, _id(case))
+    code = 1 if dtype == "bf16" else 0
+    nb = ra.ra_fwd_workspace_bytes(B, Hq, Hkv, S, d, P, True, causal, layout, code, 3)
+    ws = torch.empty(max(nb, 16), dtype=torch.uint8, device="cuda")
+    O3, L3 = torch.empty_like(O), torch.empty_like(L)
+    ra.ra_fwd_all_ws(Qs, Ks, Vs, O3, L3, P, causal, layout, 3, ws)
+    torch.cuda.synchronize()
+    check(unshard(from_dev(O3), S, P, layout, axis=1), O_ref, unshard(from_dev(L3), S, P, layout, axis=2),
+          lse_ref, dtype, _id(case) + " 3 ranges")
+    r = P - 1
+    n = S // P
+    Or, Lr = _ring_rank(Qs, Ks, Vs, S, P, r, causal, layout)
+    rows = oracle.natural_positions(S, P, layout)[r * n:(r + 1) * n]
+    check(from_dev(Or), O_ref[:, rows], from_dev(Lr), lse_ref[:, :, rows], dtype, _id(case) + " ring steps")
