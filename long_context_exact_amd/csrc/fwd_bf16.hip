@@ -154,10 +154,6 @@ struct KvTile {
     }
 };
 
-__device__ __forceinline__ i16x4 ds_read_tr(const uint16_t* p) {
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
-}
-
 // max / sum / or of a value over the two half-waves (lanes l and l^32)
 __device__ __forceinline__ float halves_max(float x) {
     const unsigned u = __builtin_bit_cast(unsigned, x);
