@@ -458,7 +458,8 @@ int ra_head_a2a(const void* src, void* dst, int64_t B, int64_t S, int P, int64_t
         return fail(RA_ERR_UNSUPPORTED, "runs of %lld bytes: need 16-byte runs and alignment",
                     (long long)run_bytes);
     const int64_t runs = (int64_t)P * B * S;
-    if ((runs + 3) / 4 > 0x7fffffffLL) return fail(RA_ERR_UNSUPPORTED, "too many runs");
+    if ((runs * ((run_bytes + 4095) / 4096) + 3) / 4 > 0x7fffffffLL)
+        return fail(RA_ERR_UNSUPPORTED, "too many runs");
     const uint8_t* s0 = (const uint8_t*)src;
     const uint8_t* d0 = (const uint8_t*)dst;
     const int64_t bytes = runs * run_bytes;

@@ -127,19 +127,24 @@ __global__ __launch_bounds__(256) void layout_rows_kernel(RowArgs a) {
 // sends head group g of its sequence shard to rank g.  With the token's heads
 // cut into P runs of run_bytes (H/P heads each), forward moves
 // [B, S, P, run] (sequence order, all heads) to [P, B, S, run] (head group
-// major: each group holds every token), inverse moves it back.  One wave per
-// destination run, enumerated in destination order, 16 bytes per lane.
+// major: each group holds every token), inverse moves it back.  Work items
+// are (destination run, 4 KiB segment of it), one wave each, enumerated in
+// destination order; lanes move 16 bytes at a time.  Long runs (an LSE row
+// of a head group is S * 4 bytes) are thus spread over many waves.
+constexpr int64_t A2A_SEG = 4096;
+
 struct A2AArgs {
     const uint8_t* src;
     uint8_t* dst;
-    int64_t B, S, runs, run_bytes;  // runs = P * B * S
+    int64_t B, S, runs, run_bytes, segs;  // runs = P * B * S; segs per run
     int P, inverse;
 };
 
 __global__ __launch_bounds__(256) void head_a2a_kernel(A2AArgs a) {
     const int lane = threadIdx.x & 63;
-    const int64_t k = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // destination run
-    if (k >= a.runs) return;
+    const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (item >= a.runs * a.segs) return;
+    const int64_t k = item / a.segs, seg = item - k * a.segs;  // destination run, segment
     int64_t srun;
     if (!a.inverse) {  // k = (g * B + b) * S + x  <-  (b * S + x) * P + g
         const int64_t g = k / (a.B * a.S), bx = k - g * a.B * a.S;
@@ -148,9 +153,12 @@ __global__ __launch_bounds__(256) void head_a2a_kernel(A2AArgs a) {
         const int64_t bx = k / a.P, g = k - bx * a.P;
         srun = g * a.B * a.S + bx;
     }
-    const uint4* s = (const uint4*)(a.src + srun * a.run_bytes);
-    uint4* d = (uint4*)(a.dst + k * a.run_bytes);
-    const int units = (int)(a.run_bytes >> 4);
+    const int64_t beg = seg * A2A_SEG;
+    int64_t len = a.run_bytes - beg;
+    if (len > A2A_SEG) len = A2A_SEG;
+    const uint4* s = (const uint4*)(a.src + srun * a.run_bytes + beg);
+    uint4* d = (uint4*)(a.dst + k * a.run_bytes + beg);
+    const int units = (int)(len >> 4);
     for (int u = lane; u < units; u += 64) d[u] = load_once16(s + u);
 }
 
@@ -166,9 +174,11 @@ hipError_t launch_head_a2a(const void* src, void* dst, int64_t B, int64_t S, int
     a.P = P;
     a.runs = (int64_t)P * B * S;
     a.run_bytes = run_bytes;
+    a.segs = (run_bytes + A2A_SEG - 1) / A2A_SEG;
     a.inverse = inverse;
-    const int64_t grid = (a.runs + 3) / 4;
+    const int64_t grid = (a.runs * a.segs + 3) / 4;
     if (grid <= 0) return hipSuccess;
+    if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
     hipLaunchKernelGGL(head_a2a_kernel, dim3((unsigned)grid), dim3(256), 0, s, a);
     return hipGetLastError();
 }

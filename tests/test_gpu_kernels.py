@@ -499,7 +499,8 @@ def test_round_robin_cache_append_and_decode(case):
 
 
 @pytest.mark.parametrize("inverse", [False, True])
-@pytest.mark.parametrize("B,S,P,run", [(2, 37, 4, 256), (1, 100, 8, 1024), (3, 5, 2, 16), (1, 9, 3, 2064)])
+@pytest.mark.parametrize("B,S,P,run", [(2, 37, 4, 256), (1, 100, 8, 1024), (3, 5, 2, 16), (1, 9, 3, 2064),
+                                       (2, 3, 4, 8240), (1, 1, 8, 65536)])  # runs over several 4 KiB segments
 def test_head_a2a_bit_exact(B, S, P, run, inverse):
     rng = np.random.default_rng([1600, B, S, P, run])
     if not inverse:
