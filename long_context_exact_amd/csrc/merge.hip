@@ -5,8 +5,9 @@
 // partial attention results in one exchange):
 //   M = max_p lse_p,  w_p = exp(lse_p - M),
 //   lse = M + ln(sum_p w_p),  O = sum_p w_p O_p / sum_p w_p.
-// One wave per row; lane j owns dims j, j+64.  The partial lse values of a
-// row are read by all lanes (a broadcast), the O partials as coalesced rows.
+// One wave per row; lane j owns dims j, j+64.  The parts' lse values are
+// read 64 at a time, one per lane, and reduced across the wave; the O
+// partials are read as coalesced rows, eight parts in flight.
 // The same kernel merges the key-range splits of the prefill, whose LSE is
 // laid out [B, Hq, rows].
 #include "ra_device.h"
@@ -14,9 +15,22 @@
 namespace ra {
 namespace {
 
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+    return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+    return x;
+}
+
 template <int D, bool LSE_BHQ>
 __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
     constexpr int EPL = D / 64;  // elements per lane
+    constexpr int U = 8;         // partial rows in flight per lane
     const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (row >= p.rows) return;
@@ -27,22 +41,43 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
         lrow = (b * p.Hq + h) * p.q_rows + q;
     }
 
+    // the parts' lse values, 64 at a time, one per lane
     float M = kNegInf;
-    for (int q = 0; q < p.n_parts; ++q) M = fmaxf(M, p.lse_parts[(int64_t)q * p.rows + lrow]);
+    for (int q0 = 0; q0 < p.n_parts; q0 += 64) {
+        const int q = q0 + lane;
+        M = fmaxf(M, q < p.n_parts ? p.lse_parts[(int64_t)q * p.rows + lrow] : kNegInf);
+    }
+    M = wave_max(M);
 
     float acc[EPL];
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
     float W = 0.f;
     if (M != kNegInf) {
-        for (int q = 0; q < p.n_parts; ++q) {
-            const float lq = p.lse_parts[(int64_t)q * p.rows + lrow];
-            if (lq == kNegInf) continue;
-            const float wq = __expf(lq - M);
-            W += wq;
-            const float* op = p.O_parts + ((int64_t)q * p.rows + row) * D;
+        for (int q0 = 0; q0 < p.n_parts; q0 += 64) {
+            const int q = q0 + lane;
+            const float lq = q < p.n_parts ? p.lse_parts[(int64_t)q * p.rows + lrow] : kNegInf;
+            const float wl = lq == kNegInf ? 0.f : __expf(lq - M);  // this lane's part weight
+            W += wave_sum(wl);
+            const int cnt = min(64, p.n_parts - q0);
+            // U independent partial rows in flight; parts of weight 0 read
+            // nothing (an empty part's O may be anything finite)
+            for (int j0 = 0; j0 < cnt; j0 += U) {
+                float wq[U], v[U][EPL];
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) acc[e] = __builtin_fmaf(wq, op[lane + 64 * e], acc[e]);
+                for (int u = 0; u < U; ++u) {
+                    const int j = j0 + u;
+                    wq[u] = __shfl(wl, j < cnt ? j : 0, 64);
+                    if (j >= cnt) wq[u] = 0.f;
+                    const float* op = p.O_parts + ((int64_t)(q0 + j) * p.rows + row) * D;
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) v[u][e] = wq[u] != 0.f ? op[lane + 64 * e] : 0.f;
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) acc[e] = __builtin_fmaf(wq[u], v[u][e], acc[e]);
+            }
         }
     }
     const float inv = W > 0.f ? 1.f / W : 0.f;
