@@ -372,7 +372,7 @@ int ra_kv_append_rr(void* K_cache, void* V_cache, const void* K_new, const void*
     if (need > cap)
         return fail(RA_ERR_INVALID_ARG, "shard 0 would hold %lld rows, capacity %lld", (long long)need,
                     (long long)cap);
-    if ((int64_t)B * n_new > 0x7fffffffLL) return fail(RA_ERR_UNSUPPORTED, "too many new rows");
+    if (((int64_t)B * n_new + 3) / 4 > 0x7fffffffLL) return fail(RA_ERR_UNSUPPORTED, "too many new rows");
     if (((uintptr_t)K_cache | (uintptr_t)V_cache | (uintptr_t)K_new | (uintptr_t)V_new) % 16 != 0)
         return fail(RA_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
     const int64_t row_bytes = (int64_t)Hkv * d * (dtype == RA_DTYPE_BF16 ? 2 : 4);

@@ -4,8 +4,8 @@
 // evenly).  Token x of the sequence is in block j = x / block, stored by
 // shard j mod P at local row (j / P) * block + x mod block.
 //
-// Pure data movement: one work-group per new (batch entry, token) row; its
-// threads copy the row's 16-byte units.  Both caches are laid out
+// Pure data movement: one wave per new (batch entry, token) row; its lanes
+// copy the row's 16-byte units.  Both caches are laid out
 // [P, B, cap, row] so each shard's cache is one contiguous region, as it
 // would be on its own device.
 #include "ra_device.h"
@@ -23,7 +23,9 @@ struct AppendArgs {
 };
 
 __global__ __launch_bounds__(256) void kv_append_rr_kernel(AppendArgs a) {
-    const int64_t id = blockIdx.x;  // b * n_new + i
+    const int64_t id = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // b * n_new + i, one wave each
+    if (id >= (int64_t)a.B * a.n_new) return;
+    const int lane = threadIdx.x & 63;
     const int64_t b = id / a.n_new, i = id - b * a.n_new;
     const int64_t x = a.len + i;    // sequence position of the new token
     const int64_t j = x / a.block;
@@ -32,9 +34,9 @@ __global__ __launch_bounds__(256) void kv_append_rr_kernel(AppendArgs a) {
     const int64_t dst = ((shard * a.B + b) * a.cap + row) * a.row_bytes;
     const int64_t src = id * a.row_bytes;
     const int units = (int)(a.row_bytes >> 4);
-    for (int u = threadIdx.x; u < units; u += 256) {
-        ((uint4*)(a.Kc + dst))[u] = ((const uint4*)(a.Kn + src))[u];
-        ((uint4*)(a.Vc + dst))[u] = ((const uint4*)(a.Vn + src))[u];
+    for (int u = lane; u < units; u += 64) {
+        ((uint4*)(a.Kc + dst))[u] = load_once16((const uint4*)(a.Kn + src) + u);
+        ((uint4*)(a.Vc + dst))[u] = load_once16((const uint4*)(a.Vn + src) + u);
     }
 }
 
@@ -55,7 +57,7 @@ hipError_t launch_kv_append_rr(void* K_cache, void* V_cache, const void* K_new, 
     a.block = block;
     a.B = B;
     a.P = P;
-    const int64_t grid = (int64_t)B * n_new;
+    const int64_t grid = ((int64_t)B * n_new + 3) / 4;
     if (grid <= 0) return hipSuccess;
     hipLaunchKernelGGL(kv_append_rr_kernel, dim3((unsigned)grid), dim3(256), 0, s, a);
     return hipGetLastError();
