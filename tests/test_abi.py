@@ -254,3 +254,21 @@ def test_valid_call_without_a_device_reports_hip_error():
     assert rc == ra.RA_ERR_HIP
     assert "launch" in ra.last_error()
     assert L.ra_merge_partials(FAKE, FAKE, FAKE, NULL, 2, 10, 128, 1, NULL) == ra.RA_ERR_HIP
+
+
+def test_header_is_plain_c(tmp_path):
+    # the ABI header compiles as C99 with warnings as errors, and a C program
+    # that takes every entry point's address links against the library
+    src = tmp_path / "use.c"
+    names = declared_symbols()
+    src.write_text('#include "ra.h"\n#include <stdio.h>\nint main(void) {\n'
+                   + "".join(f'    printf("%p\\n", (void*){n});\n' for n in names)
+                   + '    printf("%s\\n", ra_version());\n    return 0;\n}\n')
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-fsyntax-only",
+                    "-x", "c", HEADER], check=True)
+    exe = tmp_path / "use"
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror",
+                    "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe),
+                    ra.LIB_PATH, f"-Wl,-rpath,{os.path.dirname(ra.LIB_PATH)}"], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout
+    assert "gfx950" in out
