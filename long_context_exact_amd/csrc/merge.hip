@@ -93,11 +93,86 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
     if (p.lse != nullptr && lane == 0) p.lse[lrow] = W > 0.f ? M + __logf(W) : kNegInf;
 }
 
+// Few parts (the key-range splits of the prefill, 2-8 ranges): a group of
+// D/4 lanes per row, each lane owning 4 consecutive dims, so a wave merges
+// 256/D rows at once with all of a row's loads independent and no wave-wide
+// reductions.  Parts are folded in order, as above.
+constexpr int MERGE_FEW_MAX = 8;
+
+template <int D, bool LSE_BHQ>
+__global__ __launch_bounds__(256) void merge_few_kernel(MergeParams p) {
+    constexpr int LPR = D / 4;  // lanes per row
+    const int64_t row = ((int64_t)blockIdx.x * 256 + threadIdx.x) / LPR;
+    const int sub = threadIdx.x % LPR;
+    if (row >= p.rows) return;
+    int64_t lrow = row;
+    if (LSE_BHQ) {
+        const int64_t bq = row / p.Hq, h = row - bq * p.Hq;
+        const int64_t b = bq / p.q_rows, q = bq - b * p.q_rows;
+        lrow = (b * p.Hq + h) * p.q_rows + q;
+    }
+    float lq[MERGE_FEW_MAX];
+    float M = kNegInf;
+#pragma unroll
+    for (int q = 0; q < MERGE_FEW_MAX; ++q) {
+        lq[q] = q < p.n_parts ? p.lse_parts[(int64_t)q * p.rows + lrow] : kNegInf;
+        M = fmaxf(M, lq[q]);
+    }
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    float W = 0.f;
+    if (M != kNegInf) {
+        float w[MERGE_FEW_MAX];
+        float4 v[MERGE_FEW_MAX];
+#pragma unroll
+        for (int q = 0; q < MERGE_FEW_MAX; ++q) {
+            w[q] = lq[q] == kNegInf ? 0.f : __expf(lq[q] - M);
+            v[q] = w[q] != 0.f ? *(const float4*)(p.O_parts + ((int64_t)q * p.rows + row) * D + 4 * sub)
+                               : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int q = 0; q < MERGE_FEW_MAX; ++q) {
+            W += w[q];
+            acc.x = __builtin_fmaf(w[q], v[q].x, acc.x);
+            acc.y = __builtin_fmaf(w[q], v[q].y, acc.y);
+            acc.z = __builtin_fmaf(w[q], v[q].z, acc.z);
+            acc.w = __builtin_fmaf(w[q], v[q].w, acc.w);
+        }
+    }
+    const float inv = W > 0.f ? 1.f / W : 0.f;
+    if (p.out_bf16) {
+        const uint32_t lo = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(acc.x * inv)) |
+                            ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(acc.y * inv)) << 16);
+        const uint32_t hi = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(acc.z * inv)) |
+                            ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(acc.w * inv)) << 16);
+        *(uint2*)((uint16_t*)p.O + row * D + 4 * sub) = make_uint2(lo, hi);
+    } else {
+        *(float4*)((float*)p.O + row * D + 4 * sub) =
+            make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+    }
+    if (p.lse != nullptr && sub == 0) p.lse[lrow] = W > 0.f ? M + __logf(W) : kNegInf;
+}
+
 }  // namespace
 
 hipError_t launch_merge(const MergeParams& p, int d, hipStream_t s) {
+    if (p.rows <= 0) return hipSuccess;
+    // the few-parts path moves 16-byte (O partials, fp32 O) or 8-byte (bf16 O) units
+    const bool aligned = ((uintptr_t)p.O_parts | (uintptr_t)p.O) % 16 == 0;
+    if (p.n_parts <= MERGE_FEW_MAX && aligned) {
+        const int64_t grid = (p.rows * (d / 4) + 255) / 256;
+        if (p.lse_bhq) {
+            if (d == 128)
+                hipLaunchKernelGGL((merge_few_kernel<128, true>), dim3((unsigned)grid), dim3(256), 0, s, p);
+            else
+                hipLaunchKernelGGL((merge_few_kernel<64, true>), dim3((unsigned)grid), dim3(256), 0, s, p);
+        } else if (d == 128) {
+            hipLaunchKernelGGL((merge_few_kernel<128, false>), dim3((unsigned)grid), dim3(256), 0, s, p);
+        } else {
+            hipLaunchKernelGGL((merge_few_kernel<64, false>), dim3((unsigned)grid), dim3(256), 0, s, p);
+        }
+        return hipGetLastError();
+    }
     const int64_t grid = (p.rows + 3) / 4;
-    if (grid <= 0) return hipSuccess;
     if (p.lse_bhq) {
         if (d == 128)
             hipLaunchKernelGGL((merge_kernel<128, true>), dim3((unsigned)grid), dim3(256), 0, s, p);

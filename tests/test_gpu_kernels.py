@@ -183,9 +183,9 @@ def test_decode_partials_and_merge(case):
 
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("out", ["f32", "bf16"])
-def test_merge_kernel_vs_oracle(d, out):
-    rng = np.random.default_rng([1400, d])
-    n_parts, rows = 7, 1000
+@pytest.mark.parametrize("n_parts,rows", [(7, 1000), (2, 999), (70, 1000)])  # few-parts and wave paths
+def test_merge_kernel_vs_oracle(d, out, n_parts, rows):
+    rng = np.random.default_rng([1400, d, n_parts])
     Op = rng.standard_normal((n_parts, rows, d)).astype(np.float32)
     lp = (rng.standard_normal((n_parts, rows)) * 5).astype(np.float32)
     lp[rng.random((n_parts, rows)) < 0.2] = -np.inf   # empty shards
@@ -634,3 +634,19 @@ def test_prefill_random_shapes(case):
     Or, Lr = _ring_rank(Qs, Ks, Vs, S, P, r, causal, layout)
     rows = oracle.natural_positions(S, P, layout)[r * n:(r + 1) * n]
     check(from_dev(Or), O_ref[:, rows], from_dev(Lr), lse_ref[:, :, rows], dtype, _id(case) + " ring steps")
+
+
+def test_merge_unaligned_pointers():
+    # partials that start 4 bytes into an allocation take the general path
+    n_parts, rows, d = 3, 50, 64
+    rng = np.random.default_rng(1402)
+    Op = rng.standard_normal((n_parts, rows, d)).astype(np.float32)
+    lp = rng.standard_normal((n_parts, rows)).astype(np.float32)
+    big = torch.zeros(n_parts * rows * d + 1, dtype=torch.float32, device="cuda")
+    big[1:] = to_dev(Op.reshape(-1))
+    Ou = big[1:].view(n_parts, rows, d)
+    O = torch.empty(rows, d, dtype=torch.float32, device="cuda")
+    ra.ra_merge_partials(Ou, to_dev(lp), O)
+    torch.cuda.synchronize()
+    O_ref, _ = oracle.merge(Op.astype(np.float64), lp.astype(np.float64))
+    assert np.abs(from_dev(O) - O_ref).max() <= 1e-6 * max(1.0, np.abs(O_ref).max())
