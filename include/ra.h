@@ -179,7 +179,9 @@ int ra_fwd_all_ws(const void* Q, const void* K, const void* V, void* O, float* L
  * steps t > 0 fold into it and may come in any order after t = 0.  After
  * all P steps O_acc and LSE_acc equal ra_fwd_rank's fp32 output within
  * rounding (the fold reference points differ).  A bf16 copy of O_acc is
- * ra_merge_partials(O_acc, LSE_acc, O, NULL, 1, rows, d, RA_DTYPE_BF16).
+ * ra_merge_partials(O_acc, Z, O, NULL, 1, rows, d, RA_DTYPE_BF16) with Z a
+ * zero-filled fp32 array of rows = B*(S/P)*Hq entries: one part of weight 1
+ * (LSE_acc itself is laid out [B, Hq, S/P], not by row).
  * Requirements: those of ra_fwd_rank, 0 <= t < P; the state must not alias
  * Q_r or the block.  Launches of one rank's steps must be ordered (one
  * stream, or events): each reads and writes the whole state.

@@ -650,3 +650,17 @@ def test_merge_unaligned_pointers():
     torch.cuda.synchronize()
     O_ref, _ = oracle.merge(Op.astype(np.float64), lp.astype(np.float64))
     assert np.abs(from_dev(O) - O_ref).max() <= 1e-6 * max(1.0, np.abs(O_ref).max())
+
+
+def test_ring_step_state_to_bf16_as_documented():
+    # the header's recipe: one part of weight 1 rounds O_acc to bf16 exactly
+    B, S, Hq, Hkv, d, P, layout = 1, 512, 4, 2, 64, 4, "zigzag"
+    Qn, Kn, Vn = qkv(B, S, S, Hq, Hkv, d, "bf16", (1303,))
+    (Qs, Ks, Vs), _, _ = _run_prefill(Qn, Kn, Vn, P, layout, True, "bf16")
+    O, L = _ring_rank(Qs, Ks, Vs, S, P, 2, True, layout)
+    rows = O.numel() // d
+    Ob = torch.empty(O.shape, dtype=torch.bfloat16, device="cuda")
+    Z = torch.zeros(1, rows, dtype=torch.float32, device="cuda")
+    ra.ra_merge_partials(O.view(1, rows, d), Z, Ob)
+    torch.cuda.synchronize()
+    assert torch.equal(Ob.view(torch.int16), O.to(torch.bfloat16).view(torch.int16))
