@@ -664,3 +664,57 @@ def test_ring_step_state_to_bf16_as_documented():
     ra.ra_merge_partials(O.view(1, rows, d), Z, Ob)
     torch.cuda.synchronize()
     assert torch.equal(Ob.view(torch.int16), O.to(torch.bfloat16).view(torch.int16))
+
+
+def _random_decode_cases(n, seed):
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        Hkv = int(rng.choice([1, 2, 4]))
+        G = int(rng.choice([1, 2, 4, 8, 16]))
+        Sq = int(rng.integers(1, 5))
+        if Sq * G > 32:
+            continue
+        B = int(rng.integers(1, 4))
+        d = int(rng.choice([64, 128]))
+        Skv = int(rng.integers(1, 3000))
+        dtype = str(rng.choice(["bf16", "bf16", "f32"]))
+        P = int(rng.integers(1, 9))
+        block = int(rng.integers(1, 100))
+        pps = int(rng.integers(1, 10))
+        cases.append((B, Sq, Hkv * G, Hkv, d, Skv, dtype, P, block, pps))
+    return cases
+
+
+RANDOM_DECODE = _random_decode_cases(16, 1800)
+
+
+@pytest.mark.parametrize("case", RANDOM_DECODE, ids=[str(c) for c in RANDOM_DECODE])
+def test_decode_random_shapes(case):
+    """Contiguous-cache decode with P*pps parts and the same keys dealt
+    round-robin over P shard caches, both merged, against the oracle."""
+    B, Sq, Hq, Hkv, d, Skv, dtype, P, block, pps = case
+    log(f"random decode {case}")
+    Qn, Kn, Vn = qkv(B, Sq, Skv, Hq, Hkv, d, dtype, (1801, Skv, Hq, d, Sq))
+    O_ref, L_ref = oracle.attention(Qn, Kn, Vn, False)
+    rows = B * Sq * Hq
+    n_parts = P * pps
+    Qd, Kd, Vd = to_dev(Qn), to_dev(Kn), to_dev(Vn)
+    Op = torch.empty(n_parts, rows, d, dtype=torch.float32, device="cuda")
+    lp = torch.empty(n_parts, rows, dtype=torch.float32, device="cuda")
+    O = torch.empty(rows, d, dtype=torch.float32, device="cuda")
+    lse = torch.empty(rows, dtype=torch.float32, device="cuda")
+    ra.ra_attn_partial(Qd, Kd, Vd, Op, lp, n_parts)
+    ra.ra_merge_partials(Op, lp, O, lse)
+    torch.cuda.synchronize()
+    check(from_dev(O).reshape(B, Sq, Hq, d), O_ref, from_dev(lse).reshape(B, Sq, Hq).transpose(0, 2, 1),
+          L_ref, dtype, str(case) + " contiguous")
+    cap = max(len(x) for x in oracle.helix_round_robin(Skv, block, P))
+    Kc = torch.empty(P, B, cap, Hkv, d, dtype=Kd.dtype, device="cuda")
+    Vc = torch.empty_like(Kc)
+    ra.ra_kv_append_rr(Kc, Vc, Kd, Vd, 0, block)
+    ra.ra_attn_partial_rr(Qd, Kc, Vc, Op, lp, Skv, block, pps)
+    ra.ra_merge_partials(Op, lp, O, lse)
+    torch.cuda.synchronize()
+    check(from_dev(O).reshape(B, Sq, Hq, d), O_ref, from_dev(lse).reshape(B, Sq, Hq).transpose(0, 2, 1),
+          L_ref, dtype, str(case) + " round-robin")
