@@ -112,6 +112,46 @@ def cpu_baseline(w, rank: int, n_rows: int):
                       f"rows, all {w.Hq} heads, {flops / 1e9:.1f} GFLOP, {dt:.1f} s wall"}
 
 
+def sample_sclk(fn, seconds: float = 3.0):
+    """Run fn back to back for about `seconds` while a child rocm-smi samples
+    the shader clock.  Returns the MHz readings (empty without rocm-smi)."""
+    import re
+    import shutil
+    import subprocess
+    import threading
+
+    import torch
+
+    smi = shutil.which("rocm-smi")
+    if smi is None:
+        return []
+    readings = []
+
+    def sampler():
+        for _ in range(4):
+            time.sleep(seconds / 5)
+            try:
+                r = subprocess.run([smi, "--showclocks"], capture_output=True, text=True, timeout=10)
+            except (OSError, subprocess.SubprocessError):
+                continue
+            for line in r.stdout.splitlines():
+                if "sclk" in line:
+                    m = re.search(r"(\d+)\s*Mhz", line, flags=re.I)
+                    if m:
+                        readings.append(int(m.group(1)))
+                        break
+
+    th = threading.Thread(target=sampler)
+    th.start()
+    t0 = time.perf_counter()
+    while th.is_alive() and time.perf_counter() - t0 < 3 * seconds:
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+    th.join()
+    return readings
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -131,6 +171,8 @@ def main() -> int:
                     help="decode over the KV cache dealt round-robin in blocks of this many tokens "
                          "to the 8 shard caches (built by ra_kv_append_rr before timing); 0 = one "
                          "contiguous cache per sequence (default)")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip sampling the shader clock while the prefill runs back to back")
     ap.add_argument("--ulysses", action="store_true",
                     help="also time the whole prefill problem as DeepSpeed Ulysses on one GPU: "
                          "all-to-all of Q, K, V to head groups, full-sequence attention of all "
@@ -344,6 +386,18 @@ def main() -> int:
             cfg["workload"] = wd.name
     cfg["parallelism"] = "simulated ring (8 ranks resident on 1 GPU)"
     out["config"] = cfg
+    if do_pre and not args.no_clock:
+        log("sampling the shader clock while the prefill runs back to back")
+        mhz = sample_sclk(prefill)
+        if mhz:
+            med = sorted(mhz)[len(mhz) // 2]
+            attainable = PEAK_BF16_TFLOPS * med / 2400.0
+            out["roofline"]["clock"] = {
+                "sclk_mhz_samples": mhz, "sclk_mhz_median": med,
+                "peak_at_this_clock_tflops": attainable,
+                "frac_at_this_clock": out["roofline"]["achieved"] / attainable,
+                "note": "rocm-smi in a child process while the rank share runs back to back; the "
+                        "published peak is quoted at 2400 MHz"}
     if do_pre and args.all_ranks:
         log(f"timing each of the {wp.P} ranks, {args.steps} launches each")
         per = []
