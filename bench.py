@@ -490,13 +490,26 @@ def main() -> int:
             torch.cuda.synchronize()
             return e0.elapsed_time(e1) / args.steps
 
+        t_graph = None
         if wp.B == 1:  # a shard of a [1, S, H, d] tensor is a contiguous block
             t_res = time_fn(steps_resident)
+            # the same P launches captured once and replayed (no allocation, no memset inside)
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                steps_resident()
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=side):
+                steps_resident()
+            torch.cuda.synchronize()
+            t_graph = time_fn(graph.replay)
         else:
             t_res = None
         t_db = time_fn(steps_double_buffered)
         blk_bytes = 2 * bufK[0].numel() * bufK[0].element_size()
-        out["ring_steps"] = {"steps": wp.P, "resident_ms": t_res, "double_buffered_ms": t_db,
+        out["ring_steps"] = {"steps": wp.P, "resident_ms": t_res, "graph_replay_ms": t_graph,
+                             "double_buffered_ms": t_db,
                              "fused_ms": ms["prefill"], "block_bytes_per_step": blk_bytes,
                              "overhead_vs_fused": t_db / ms["prefill"] - 1.0}
         del O_s, L_s, bufK, bufV
