@@ -18,9 +18,10 @@
 // Reference point.  O and l are kept relative to a reference m' that only
 // has to keep the exponentials in range, not equal the running maximum: a
 // tile whose 32 exponentials (per lane) sum to at most 2^8 is accepted as it
-// is, so most tiles need no max reduction and no O rescale.  Otherwise (and
-// until a lane has seen a finite score) the slow path takes the true maximum,
-// rescales l and O by a = exp2(m' - m'') and recomputes the tile's P.
+// is, so most tiles need no max reduction and no O rescale.  Otherwise (also
+// at a lane's first finite score, which overflows the sum against the initial
+// reference) the slow path takes the true maximum, rescales l and O by
+// a = exp2(m' - m'') and recomputes the tile's P.
 //
 // The score matrix is produced transposed (keys along MFMA rows, queries
 // along columns) so each lane holds whole rows of its own query.  The K rows
@@ -51,6 +52,10 @@ constexpr int NW = 8;                 // waves per work-group
 constexpr int NT = 64 * NW;           // threads per work-group
 constexpr int NBUF = 4;               // LDS ring depth (K and V rings stay below 64 KB each)
 constexpr float kSumCap = 256.f;      // largest accepted per-lane tile sum of P
+// Initial reference point: finite, so the stage needs no -inf test.  Any
+// finite score then overflows the tile sum to +inf and takes the slow path,
+// where the rescale factor exp2(kRefInit - m'') is 0.
+constexpr float kRefInit = -1e30f;
 static_assert(BM == 32 * NW, "32 queries per wave");
 
 #ifndef RA_FWD_AHEAD
@@ -330,7 +335,7 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdParams p) {
     for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
-    float m_ref = kNegInf, l_run = 0.f, lr_run = 0.f;
+    float m_ref = kRefInit, l_run = 0.f, lr_run = 0.f;
     f32x16 zero16;
 #pragma unroll
     for (int r = 0; r < 16; ++r) zero16[r] = 0.f;
@@ -452,7 +457,7 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdParams p) {
             // recompute the operand addresses in every stage rather than hold
             // twelve of them in registers
             asm volatile("" : "+v"(kbase), "+v"(vbase));
-            const float mu = m_ref == kNegInf ? 0.f : m_ref;
+            const float mu = m_ref;
             const bf16x2 kOnes = {(__bf16)1.0f, (__bf16)1.0f};
             constexpr int NE = 32;            // softmax elements per lane and tile
             constexpr int EPS = NE / NMF;     // elements per MFMA slot
@@ -484,7 +489,7 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdParams p) {
                     if (e1 < NE) tf[e1] = __builtin_fmaf(sval(e1), c, -mu);
                     if (e0 < NE) ex[e0] = fast_exp2(tf[e0]);
                     if (em >= 0 && em < NE) {
-                        lsum += ex[em];
+                        lsum = em == 0 ? ex[0] : lsum + ex[em];
                         if (em & 1) {
                             bf16x2 pr;
                             pr[0] = (__bf16)ex[em - 1];
@@ -499,7 +504,7 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdParams p) {
             }
         }
         // rare: a lane's sum exceeded the cap, or its first finite score
-        const bool slow = lsum > kSumCap || (m_ref == kNegInf && lsum > 0.f);
+        const bool slow = lsum > kSumCap;
         if (__builtin_amdgcn_ballot_w64(slow) != 0) {
             const bool need = halves_any(slow);
             float mx = kNegInf;
@@ -509,7 +514,7 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdParams p) {
                 for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb2][r]);
             mx = halves_max(mx) * c;
             const float m_new = need ? fmaxf(m_ref, mx) : m_ref;
-            const float alpha = need ? fast_exp2(m_ref - m_new) : 1.f;  // 0 when m was -inf
+            const float alpha = need ? fast_exp2(m_ref - m_new) : 1.f;  // 0 at the first finite score
             l_run *= alpha;
             lr_run *= alpha;
 #pragma unroll
@@ -517,7 +522,7 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
             m_ref = m_new;
-            exp_tile(sc, c, m_new == kNegInf ? 0.f : m_new, pc, lsum, lrsum);
+            exp_tile(sc, c, m_new, pc, lsum, lrsum);
         }
         l_run += lsum;
         lr_run += lrsum;
