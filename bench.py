@@ -114,7 +114,9 @@ def cpu_baseline(w, rank: int, n_rows: int):
 
 def sample_sclk(fn, seconds: float = 3.0):
     """Run fn back to back for about `seconds` while a child rocm-smi samples
-    the shader clock.  Returns the MHz readings (empty without rocm-smi)."""
+    the shader clock.  Returns the MHz readings (empty without rocm-smi, and
+    under rocprofv3, whose tool library would initialise the GPU in the child
+    before rocm-smi's interpreter starts)."""
     import re
     import shutil
     import subprocess
@@ -123,7 +125,7 @@ def sample_sclk(fn, seconds: float = 3.0):
     import torch
 
     smi = shutil.which("rocm-smi")
-    if smi is None:
+    if smi is None or any(k.startswith("ROCPROF") for k in os.environ):
         return []
     readings = []
 
