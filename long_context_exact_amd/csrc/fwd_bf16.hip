@@ -31,14 +31,16 @@
 // row-major in LDS; its A operand (8 consecutive keys of one head dim per
 // lane) comes from two ds_read_b64_tr_b16 transposing reads.
 //
-// Schedule.  A wave issues independent VALU work behind its own MFMAs almost
-// for free, so every wave software-pipelines its own loop: in iteration i it
-// issues the MFMAs of S_{i+1} = K_{i+1} Q^T and O += V_{i-1} P_{i-1} and, in
-// between them, the softmax of S_i.  K/V tiles go from global memory straight
-// into a ring of four LDS buffers (global_load_lds_dwordx4, no staging
-// registers), two tiles ahead of the tile whose scores are being formed.  The
-// loop body is unrolled over the ring so that every LDS operand address is a
-// per-lane base plus an immediate offset.
+// Schedule.  A wave hides part of its independent VALU work behind its own
+// MFMAs (the two pipes overlap only in part), so every wave software-pipelines
+// its own loop: in iteration i it issues the MFMAs of S_{i+1} = K_{i+1} Q^T and
+// O += V_{i-1} P_{i-1} and, in between them, the softmax of S_i.  The stage
+// opens with a PV product whose V operand was read before the barrier, so an
+// MFMA is in flight while the K operands arrive and the next loads go out.
+// K/V tiles go from global memory straight into a ring of four LDS buffers
+// (global_load_lds_dwordx4, no staging registers), two tiles ahead of the tile
+// whose scores are being formed.  The loop body is unrolled over the ring so
+// that every LDS operand address is a per-lane base plus an immediate offset.
 #include <type_traits>
 
 #include "ra_device.h"
@@ -412,6 +414,9 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdParams p) {
     else
         __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
+    // V operand 0 of the next stage's first MFMA (a PV product), read before
+    // the barrier that opens the stage: V of tile i-1 has long been resident
+    bf16x8 vpre = read_v(0, NBUF - 1);
     if (n > 0) {
 #pragma unroll
         for (int j = 0; j < NQK; ++j) {
@@ -432,12 +437,6 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdParams p) {
         // tile i+1 resident; the buffer of tile i-2 is free for tile i+2
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         __syncthreads();
-        if (issued < n) {
-            cur_next(p, qt.rank, qmax, it_l);
-            T::load(Kg + it_l.krow * row_stride, Vg + it_l.krow * row_stride, offs, min(it_l.cleft, BN),
-                    row_bytes, ldsK[(SLOT + 2) % NBUF], ldsV[(SLOT + 2) % NBUF], w, lane);
-            ++issued;
-        }
         // S_{i+1} from buffer (i+1) (stale data past the last tile: unused)
         constexpr int KBUF = (SLOT + 1) % NBUF, VBUF = (SLOT + NBUF - 1) % NBUF;
 
@@ -446,8 +445,8 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdParams p) {
             const int lim = p.causal ? min(max(qpos - it_c.kpos + 1, 0), klen) : klen;
             mask_tile(sc, lim - 8 * h);
         }
-        // The stage, slot by slot: MFMA slot j is QK operand j/2 (even j) or
-        // PV operand j/2 (odd j); behind it the softmax runs one element per
+        // The stage, slot by slot: MFMA slot j is PV operand j/2 (even j) or
+        // QK operand j/2 (odd j); behind it the softmax runs one element per
         // slot as a three-step pipeline (FMA of element j+1, exp of element
         // j, sums and bf16 packing of element j-1), so exactly one exp and
         // about three other VALU instructions trail each MFMA and only a few
@@ -462,26 +461,33 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdParams p) {
             constexpr int NE = 32;            // softmax elements per lane and tile
             constexpr int EPS = NE / NMF;     // elements per MFMA slot
             static_assert(NQK == NPV && EPS * NMF == NE, "slot layout");
-            auto read_op = [&](int j) -> bf16x8 { return (j & 1) ? read_v(j >> 1, VBUF) : read_k(j >> 1, KBUF); };
+            auto read_op = [&](int j) -> bf16x8 { return (j & 1) ? read_k(j >> 1, KBUF) : read_v(j >> 1, VBUF); };
             auto sval = [&](int e) -> float { return sc[e >> 4][e & 15]; };
             float tf[NE], ex[NE];
             bf16x8 ops[AHEAD];
 #pragma unroll
-            for (int j = 0; j < AHEAD; ++j) ops[j] = read_op(j);
+            for (int j = 1; j <= AHEAD; ++j) ops[j % AHEAD] = read_op(j);
 #pragma unroll
             for (int q = 0; q < EPS; ++q) tf[q] = __builtin_fmaf(sval(q), c, -mu);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int j = 0; j <= NMF; ++j) {
                 if (j < NMF) {
-                    const bf16x8 a = ops[j % AHEAD];
+                    const bf16x8 a = j == 0 ? vpre : ops[j % AHEAD];
                     const int q = j >> 1;
-                    if ((j & 1) == 0)
+                    if ((j & 1) == 1)
                         sn[q & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[q >> 1], q < 2 ? zero16 : sn[q & 1],
                                                                             0, 0, 0);
                     else
                         oacc[q % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pp[q / DB], oacc[q % DB], 0, 0, 0);
-                    if (j + AHEAD < NMF) ops[j % AHEAD] = read_op(j + AHEAD);
+                    if (j >= 1 && j + AHEAD < NMF) ops[j % AHEAD] = read_op(j + AHEAD);
+                    // the next tile's loads go out behind the first MFMA
+                    if (j == 0 && issued < n) {
+                        cur_next(p, qt.rank, qmax, it_l);
+                        T::load(Kg + it_l.krow * row_stride, Vg + it_l.krow * row_stride, offs, min(it_l.cleft, BN),
+                                row_bytes, ldsK[(SLOT + 2) % NBUF], ldsV[(SLOT + 2) % NBUF], w, lane);
+                        ++issued;
+                    }
                 }
 #pragma unroll
                 for (int q = 0; q < EPS; ++q) {
@@ -527,6 +533,7 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdParams p) {
         l_run += lsum;
         lr_run += lrsum;
         if (i + 1 < n) cur_next(p, qt.rank, qmax, it_c);
+        vpre = read_v(0, SLOT);
     };
 
     static_assert(NBUF == 4, "the loop body is unrolled over the ring");
