@@ -447,11 +447,16 @@ def main() -> int:
         def block(x, s_):
             return x[:, s_ * n:(s_ + 1) * n]
 
-        def steps_resident():
+        def step_plain(Kb, Vb, t):
+            ra.ra_ring_step(Q_rc, Kb, Vb, O_s, L_s, wp.S, wp.P, r, t, wp.causal, wp.layout)
+
+        def step_split(Kb, Vb, t):  # automatic key-range splits through the rank's workspace
+            ra.ra_ring_step_ws(Q_rc, Kb, Vb, O_s, L_s, wp.S, wp.P, r, t, wp.causal, wp.layout, 0, ws_r)
+
+        def steps_resident(step=step_plain):
             for t in range(wp.P):
                 s_ = (r - t) % wp.P
-                ra.ra_ring_step(Q_rc, block(Ks, s_), block(Vs, s_), O_s, L_s, wp.S, wp.P, r, t,
-                                wp.causal, wp.layout)
+                step(block(Ks, s_), block(Vs, s_), t)
 
         comp = torch.cuda.current_stream()
         copy = torch.cuda.Stream()
@@ -468,7 +473,7 @@ def main() -> int:
                 bufV[t % 2].copy_(block(Vs, s_))
                 arrived[t % 2].record(copy)
 
-        def steps_double_buffered():
+        def steps_double_buffered(step=step_plain):
             for e in free:
                 e.record(comp)
             receive(0)
@@ -476,8 +481,7 @@ def main() -> int:
                 if t + 1 < wp.P:
                     receive(t + 1)
                 comp.wait_event(arrived[t % 2])
-                ra.ra_ring_step(Q_rc, bufK[t % 2], bufV[t % 2], O_s, L_s, wp.S, wp.P, r, t,
-                                wp.causal, wp.layout)
+                step(bufK[t % 2], bufV[t % 2], t)
                 free[t % 2].record(comp)
 
         def time_fn(fn):
@@ -492,9 +496,10 @@ def main() -> int:
             torch.cuda.synchronize()
             return e0.elapsed_time(e1) / args.steps
 
-        t_graph = None
+        t_graph = t_res_split = None
         if wp.B == 1:  # a shard of a [1, S, H, d] tensor is a contiguous block
             t_res = time_fn(steps_resident)
+            t_res_split = time_fn(lambda: steps_resident(step_split))
             # the same P launches captured once and replayed (no allocation, no memset inside)
             side = torch.cuda.Stream()
             side.wait_stream(torch.cuda.current_stream())
@@ -509,11 +514,17 @@ def main() -> int:
         else:
             t_res = None
         t_db = time_fn(steps_double_buffered)
+        t_db_split = time_fn(lambda: steps_double_buffered(step_split))
         blk_bytes = 2 * bufK[0].numel() * bufK[0].element_size()
         out["ring_steps"] = {"steps": wp.P, "resident_ms": t_res, "graph_replay_ms": t_graph,
                              "double_buffered_ms": t_db,
                              "fused_ms": ms["prefill"], "block_bytes_per_step": blk_bytes,
-                             "overhead_vs_fused": t_db / ms["prefill"] - 1.0}
+                             "overhead_vs_fused": t_db / ms["prefill"] - 1.0,
+                             # the library's automatic count for a step: the rank share's,
+                             # capped at one range per 1024 keys of the block
+                             "kv_splits": max(1, min(splits_r, n // 1024)), "resident_split_ms": t_res_split,
+                             "double_buffered_split_ms": t_db_split,
+                             "overhead_vs_fused_split": t_db_split / ms["prefill"] - 1.0}
         del O_s, L_s, bufK, bufV
     if do_pre and args.ulysses:
         P_, B_, S_ = wp.P, wp.B, wp.S

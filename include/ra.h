@@ -191,9 +191,40 @@ int ra_ring_step(const void* Q_r, const void* K_blk, const void* V_blk, float* O
                  int t, int causal, int layout, int dtype, void* stream);
 
 /*
- * ra_fwd_workspace_bytes -- workspace that ra_fwd_rank_ws (all_ranks = 0) or
- * ra_fwd_all_ws (all_ranks = 1) needs for kv_splits ranges (0: the automatic
- * choice): kv_splits * rows * (d + 1) * 4 bytes with rows = B * Hq * (S/P or S),
+ * ra_ring_step_ws -- ra_ring_step with key-range splits, for steps whose
+ * launch has too few query tiles to fill the GPU (under the causal split,
+ * steps t > 0 give work to only some of a rank's tiles).  Each tile's key
+ * tiles of the block are cut into kv_splits contiguous ranges, one
+ * work-group each, whose fp32 (O, lse) partials go to `workspace`; one merge
+ * then folds the ranges and, for t > 0, the running state (as its first
+ * part) into (O_acc, LSE_acc), in place ([L8] section 3 applied to the
+ * ranges and the state).
+ *   kv_splits: 0 = automatic (about two work-groups per compute unit, at
+ *              most 8 and at most one per 1024 keys of the block, fewer if
+ *              the workspace is smaller), 1..64 = exactly that many
+ *              (RA_ERR_INVALID_ARG if the workspace is too small).
+ *   workspace: device memory owned by the caller, 16-byte aligned, of
+ *              ra_fwd_workspace_bytes(..., all_ranks = 0, ...) bytes for the
+ *              same shape and kv_splits (enough for the automatic choice);
+ *              NULL with workspace_bytes = 0 runs one range.
+ * With one range it is ra_ring_step exactly (bit for bit).  The ranges cost
+ * a merge launch and fp32 traffic per step (partials and the state), so
+ * they pay only when a step leaves compute units idle and its block is
+ * large enough.  Other counts
+ * agree with it within rounding.  Requirements and ordering: those of
+ * ra_ring_step; the workspace must not alias any tensor, and calls that
+ * share it must be ordered.
+ */
+int ra_ring_step_ws(const void* Q_r, const void* K_blk, const void* V_blk, float* O_acc,
+                    float* LSE_acc, int B, int Hq, int Hkv, int64_t S, int d, int P, int rank,
+                    int t, int causal, int layout, int dtype, int kv_splits, void* workspace,
+                    int64_t workspace_bytes, void* stream);
+
+/*
+ * ra_fwd_workspace_bytes -- workspace that ra_fwd_rank_ws and ra_ring_step_ws
+ * (all_ranks = 0) or ra_fwd_all_ws (all_ranks = 1) need for kv_splits ranges
+ * (0: the automatic choice): kv_splits * rows * (d + 1) * 4 bytes with
+ * rows = B * Hq * (S/P or S),
  * 0 for one range.  Returns a negative ra_status for invalid shapes.  No HIP
  * call is made.
  */

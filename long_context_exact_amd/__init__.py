@@ -28,7 +28,7 @@ def layout_zigzag_k(k: int) -> int:
 DTYPE_F32, DTYPE_BF16 = 0, 1
 
 EXPORTS = ("ra_fwd_rank", "ra_fwd_all", "ra_fwd_rank_ws", "ra_fwd_all_ws", "ra_fwd_workspace_bytes",
-           "ra_ring_step", "ra_kv_append_rr", "ra_attn_partial_rr", "ra_head_a2a",
+           "ra_ring_step", "ra_ring_step_ws", "ra_kv_append_rr", "ra_attn_partial_rr", "ra_head_a2a",
            "ra_merge_partials", "ra_attn_partial",
            "ra_layout_gather", "ra_last_error", "ra_version")
 
@@ -61,6 +61,8 @@ def lib() -> ctypes.CDLL:
         L.ra_fwd_workspace_bytes.argtypes = [i32, i32, i32, i64, i32, i32, i32, i32, i32, i32, i32]
         L.ra_ring_step.argtypes = [vp, vp, vp, fp, fp, i32, i32, i32, i64, i32, i32, i32, i32, i32,
                                    i32, i32, vp]
+        L.ra_ring_step_ws.argtypes = [vp, vp, vp, fp, fp, i32, i32, i32, i64, i32, i32, i32, i32, i32,
+                                      i32, i32, i32, vp, i64, vp]
         L.ra_head_a2a.argtypes = [vp, vp, i64, i64, i32, i64, i32, vp]
         L.ra_kv_append_rr.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i64, i64, i64, i64, i32, vp]
         L.ra_attn_partial_rr.argtypes = [vp, vp, vp, fp, fp, i32, i32, i32, i64, i64, i64, i64, i32,
@@ -69,7 +71,7 @@ def lib() -> ctypes.CDLL:
         L.ra_merge_partials.argtypes = [fp, fp, vp, fp, i32, i64, i32, i32, vp]
         L.ra_attn_partial.argtypes = [vp, vp, vp, fp, fp, i32, i32, i32, i64, i64, i32, i32, i32, vp]
         L.ra_layout_gather.argtypes = [vp, vp, i64, i64, i64, i32, i32, i32, vp]
-        for f in ("ra_fwd_rank", "ra_fwd_all", "ra_fwd_rank_ws", "ra_fwd_all_ws", "ra_ring_step",
+        for f in ("ra_fwd_rank", "ra_fwd_all", "ra_fwd_rank_ws", "ra_fwd_all_ws", "ra_ring_step", "ra_ring_step_ws",
                   "ra_kv_append_rr", "ra_attn_partial_rr", "ra_head_a2a",
                   "ra_merge_partials", "ra_attn_partial", "ra_layout_gather"):
             getattr(L, f).restype = ctypes.c_int
@@ -220,11 +222,7 @@ def ra_fwd_all_ws(Q, K, V, O, LSE, P: int, causal: bool, layout, kv_splits: int 
                                _stream(stream)))
 
 
-def ra_ring_step(Q_r, K_blk, V_blk, O_acc, LSE_acc, S: int, P: int, rank: int, t: int,
-                 causal: bool, layout, stream=None):
-    """One ring step: fold the block of shard (rank - t) mod P (K_blk, V_blk
-    [B, S/P, Hkv, d]) into the running fp32 state O_acc [B, S/P, Hq, d],
-    LSE_acc [B, Hq, S/P] of the rank's queries Q_r [B, S/P, Hq, d]."""
+def _ring_step_args(Q_r, K_blk, V_blk, O_acc, LSE_acc, S, P, rank, t, causal, layout):
     B, n, Hkv, d = K_blk.shape
     Hq = Q_r.shape[2]
     torch = _torch()
@@ -236,10 +234,28 @@ def ra_ring_step(Q_r, K_blk, V_blk, O_acc, LSE_acc, S: int, P: int, rank: int, t
         raise ValueError("LSE_acc must be float32 [B, Hq, S/P]")
     if not (K_blk.dtype == V_blk.dtype == Q_r.dtype):
         raise TypeError("Q, K, V must share a dtype")
-    _check(lib().ra_ring_step(_dev(Q_r, "Q_r"), _dev(K_blk, "K_blk"), _dev(V_blk, "V_blk"),
-                              _dev(O_acc, "O_acc"), _dev(LSE_acc, "LSE_acc"), B, Hq, Hkv, S, d, P,
-                              rank, t, int(bool(causal)), _layout(layout), _dtype_code(Q_r),
-                              _stream(stream)))
+    return (_dev(Q_r, "Q_r"), _dev(K_blk, "K_blk"), _dev(V_blk, "V_blk"), _dev(O_acc, "O_acc"),
+            _dev(LSE_acc, "LSE_acc"), B, Hq, Hkv, S, d, P, rank, t, int(bool(causal)), _layout(layout),
+            _dtype_code(Q_r))
+
+
+def ra_ring_step(Q_r, K_blk, V_blk, O_acc, LSE_acc, S: int, P: int, rank: int, t: int,
+                 causal: bool, layout, stream=None):
+    """One ring step: fold the block of shard (rank - t) mod P (K_blk, V_blk
+    [B, S/P, Hkv, d]) into the running fp32 state O_acc [B, S/P, Hq, d],
+    LSE_acc [B, Hq, S/P] of the rank's queries Q_r [B, S/P, Hq, d]."""
+    args = _ring_step_args(Q_r, K_blk, V_blk, O_acc, LSE_acc, S, P, rank, t, causal, layout)
+    _check(lib().ra_ring_step(*args, _stream(stream)))
+
+
+def ra_ring_step_ws(Q_r, K_blk, V_blk, O_acc, LSE_acc, S: int, P: int, rank: int, t: int,
+                    causal: bool, layout, kv_splits: int = 0, workspace=None, stream=None):
+    """ra_ring_step with key-range splits merged, with the running state,
+    through ``workspace`` (a device tensor of at least
+    ra_fwd_workspace_bytes(..., all_ranks=False, ...) bytes, or None)."""
+    args = _ring_step_args(Q_r, K_blk, V_blk, O_acc, LSE_acc, S, P, rank, t, causal, layout)
+    wp, wb = _ws(workspace)
+    _check(lib().ra_ring_step_ws(*args, int(kv_splits), wp, wb, _stream(stream)))
 
 
 def ra_kv_append_rr(K_cache, V_cache, K_new, V_new, length: int, block: int, stream=None):

@@ -149,6 +149,10 @@ int launch_fwd(const ra::FwdParams& p, int d, int dtype, void* stream) {
 // balance gains (8 ranges beat 16 on a 32-tile rank share).
 constexpr int kComputeUnits = 256;  // MI355X
 constexpr int kAutoMaxSplits = 8;
+// One ring step covers one block of S/P keys.  On the 8k-token workload
+// (1024-key blocks) eight automatic ranges made the steps 28% slower; on the
+// 32k one (4096-key blocks) two ranges made them 9% faster.
+constexpr int64_t kAutoMinRangeKeys = 1024;
 
 int64_t fwd_units(const ra::FwdParams& p) {
     return (int64_t)p.n_ranks * p.chunks_per_rank * p.tiles_per_chunk * p.B * p.Hq;
@@ -170,7 +174,7 @@ int64_t split_bytes(const ra::FwdParams& p, int d, int splits) {
 }
 
 int fwd_split(ra::FwdParams p, int d, int dtype, int o_dtype, int kv_splits, void* ws,
-              int64_t ws_bytes, void* stream) {
+              int64_t ws_bytes, void* stream, int max_auto = kAutoMaxSplits) {
     if (kv_splits < 0 || kv_splits > RA_MAX_KV_SPLITS)
         return fail(RA_ERR_INVALID_ARG, "kv_splits=%d outside [0, %d]", kv_splits, RA_MAX_KV_SPLITS);
     if (ws_bytes < 0) return fail(RA_ERR_INVALID_ARG, "negative workspace size");
@@ -178,6 +182,7 @@ int fwd_split(ra::FwdParams p, int d, int dtype, int o_dtype, int kv_splits, voi
     int splits = kv_splits;
     if (splits == 0) {
         splits = auto_splits(p);
+        if (splits > max_auto) splits = max_auto;
         while (splits > 1 && split_bytes(p, d, splits) > ws_bytes) --splits;
     } else if (split_bytes(p, d, splits) > ws_bytes) {
         return fail(RA_ERR_INVALID_ARG, "workspace of %lld bytes, %d splits need %lld",
@@ -185,6 +190,10 @@ int fwd_split(ra::FwdParams p, int d, int dtype, int o_dtype, int kv_splits, voi
     }
     if (splits == 1) return launch_fwd(p, d, dtype, stream);
     if ((uintptr_t)ws % 16 != 0) return fail(RA_ERR_INVALID_ARG, "workspace not 16-byte aligned");
+    // a ring step past the first folds its ranges and the running state in
+    // one merge (the state as its first part, written back in place)
+    const int fold = p.fold;
+    p.fold = 0;
     const int64_t rows = (int64_t)p.B * p.q_rows * p.Hq;
     if ((rows + 3) / 4 > 0x7fffffffLL) return fail(RA_ERR_UNSUPPORTED, "too many rows");
     float* o_parts = (float*)ws;
@@ -211,6 +220,8 @@ int fwd_split(ra::FwdParams p, int d, int dtype, int o_dtype, int kv_splits, voi
     m.lse_bhq = 1;
     m.q_rows = p.q_rows;
     m.Hq = p.Hq;
+    m.O_state = fold ? (const float*)O : nullptr;
+    m.lse_state = fold ? LSE : nullptr;
     return hip_status(ra::launch_merge(m, d, (hipStream_t)stream), "merge kernel launch");
 }
 
@@ -264,6 +275,14 @@ int ra_fwd_all_ws(const void* Q, const void* K, const void* V, void* O, float* L
 int ra_ring_step(const void* Q_r, const void* K_blk, const void* V_blk, float* O_acc, float* LSE_acc,
                  int B, int Hq, int Hkv, int64_t S, int d, int P, int rank, int t, int causal,
                  int layout, int dtype, void* stream) {
+    return ra_ring_step_ws(Q_r, K_blk, V_blk, O_acc, LSE_acc, B, Hq, Hkv, S, d, P, rank, t, causal, layout,
+                           dtype, 1, nullptr, 0, stream);
+}
+
+int ra_ring_step_ws(const void* Q_r, const void* K_blk, const void* V_blk, float* O_acc, float* LSE_acc,
+                    int B, int Hq, int Hkv, int64_t S, int d, int P, int rank, int t, int causal,
+                    int layout, int dtype, int kv_splits, void* workspace, int64_t workspace_bytes,
+                    void* stream) {
     int rc = check_fwd(Q_r, K_blk, V_blk, O_acc, LSE_acc, B, Hq, Hkv, S, d, P, causal, layout, dtype,
                        RA_DTYPE_F32);
     if (rc != RA_OK) return rc;
@@ -276,7 +295,11 @@ int ra_ring_step(const void* Q_r, const void* K_blk, const void* V_blk, float* O
     p.kv_block = 1;
     p.kv_rows = p.n;
     p.fold = t > 0;
-    return launch_fwd(p, d, dtype, stream);
+    // automatic ranges of at least 1024 keys of the block: below that the
+    // partials and the merge cost more than the balance gains
+    const int64_t max_auto = p.n / kAutoMinRangeKeys;
+    return fwd_split(p, d, dtype, RA_DTYPE_F32, kv_splits, workspace, workspace_bytes, stream,
+                     (int)(max_auto < 1 ? 1 : max_auto < kAutoMaxSplits ? max_auto : kAutoMaxSplits));
 }
 
 int64_t ra_fwd_workspace_bytes(int B, int Hq, int Hkv, int64_t S, int d, int P, int all_ranks,
@@ -316,6 +339,8 @@ int ra_merge_partials(const float* O_parts, const float* lse_parts, void* O, flo
     p.lse_bhq = 0;
     p.q_rows = 0;
     p.Hq = 1;
+    p.O_state = nullptr;
+    p.lse_state = nullptr;
     return hip_status(ra::launch_merge(p, d, (hipStream_t)stream), "merge kernel launch");
 }
 

@@ -9,7 +9,9 @@
 // read 64 at a time, one per lane, and reduced across the wave; the O
 // partials are read as coalesced rows, eight parts in flight.
 // The same kernel merges the key-range splits of the prefill, whose LSE is
-// laid out [B, Hq, rows].
+// laid out [B, Hq, rows], and, for a split ring step, folds them into the
+// running state as one more part (the state first), in place: every lane of
+// a row reads the row's state before the row's wave writes it.
 #include "ra_device.h"
 
 namespace ra {
@@ -41,19 +43,27 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
         lrow = (b * p.Hq + h) * p.q_rows + q;
     }
 
-    // the parts' lse values, 64 at a time, one per lane
+    // the parts' lse values, 64 at a time, one per lane (and the state's)
+    const float ls = p.lse_state != nullptr ? p.lse_state[lrow] : kNegInf;
     float M = kNegInf;
     for (int q0 = 0; q0 < p.n_parts; q0 += 64) {
         const int q = q0 + lane;
         M = fmaxf(M, q < p.n_parts ? p.lse_parts[(int64_t)q * p.rows + lrow] : kNegInf);
     }
-    M = wave_max(M);
+    M = fmaxf(wave_max(M), ls);
 
     float acc[EPL];
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
     float W = 0.f;
     if (M != kNegInf) {
+        if (ls != kNegInf) {  // the state first
+            const float ws = __expf(ls - M);
+            const float* op = p.O_state + row * D;
+            W = ws;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) acc[e] = ws * op[lane + 64 * e];
+        }
         for (int q0 = 0; q0 < p.n_parts; q0 += 64) {
             const int q = q0 + lane;
             const float lq = q < p.n_parts ? p.lse_parts[(int64_t)q * p.rows + lrow] : kNegInf;
@@ -112,7 +122,8 @@ __global__ __launch_bounds__(256) void merge_few_kernel(MergeParams p) {
         lrow = (b * p.Hq + h) * p.q_rows + q;
     }
     float lq[MERGE_FEW_MAX];
-    float M = kNegInf;
+    const float ls = p.lse_state != nullptr ? p.lse_state[lrow] : kNegInf;
+    float M = ls;
 #pragma unroll
     for (int q = 0; q < MERGE_FEW_MAX; ++q) {
         lq[q] = q < p.n_parts ? p.lse_parts[(int64_t)q * p.rows + lrow] : kNegInf;
@@ -121,6 +132,12 @@ __global__ __launch_bounds__(256) void merge_few_kernel(MergeParams p) {
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     float W = 0.f;
     if (M != kNegInf) {
+        if (ls != kNegInf) {  // the state first
+            const float ws = __expf(ls - M);
+            const float4 s4 = *(const float4*)(p.O_state + row * D + 4 * sub);
+            W = ws;
+            acc = make_float4(ws * s4.x, ws * s4.y, ws * s4.z, ws * s4.w);
+        }
         float w[MERGE_FEW_MAX];
         float4 v[MERGE_FEW_MAX];
 #pragma unroll
@@ -157,7 +174,7 @@ __global__ __launch_bounds__(256) void merge_few_kernel(MergeParams p) {
 hipError_t launch_merge(const MergeParams& p, int d, hipStream_t s) {
     if (p.rows <= 0) return hipSuccess;
     // the few-parts path moves 16-byte (O partials, fp32 O) or 8-byte (bf16 O) units
-    const bool aligned = ((uintptr_t)p.O_parts | (uintptr_t)p.O) % 16 == 0;
+    const bool aligned = ((uintptr_t)p.O_parts | (uintptr_t)p.O | (uintptr_t)p.O_state) % 16 == 0;
     if (p.n_parts <= MERGE_FEW_MAX && aligned) {
         const int64_t grid = (p.rows * (d / 4) + 255) / 256;
         if (p.lse_bhq) {

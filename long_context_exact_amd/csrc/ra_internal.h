@@ -95,6 +95,11 @@ struct MergeParams {
     int lse_bhq;
     int64_t q_rows;
     int Hq;
+    // optional running state, folded in as a first part and overwritten in
+    // place: O_state (fp32 rows x d) is then also O, lse_state (laid out like
+    // lse) also lse; null when there is none
+    const float* O_state;
+    const float* lse_state;
 };
 
 // Launchers (each returns hipSuccess or the launch error).

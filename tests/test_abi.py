@@ -197,6 +197,30 @@ def test_ring_step_rejects_before_the_device():
 
 
 @cpu_only
+def test_ring_step_ws_rejects_before_the_device():
+    L = ra.lib()
+
+    def call(kv_splits, ws=NULL, ws_bytes=0, t=1, rank=0, **kw):
+        a = dict(B=1, Hq=8, Hkv=8, S=8192, d=128, P=8, causal=1, layout=1, dtype=1)
+        a.update(kw)
+        return L.ra_ring_step_ws(FAKE, FAKE, FAKE, FAKE, FAKE, a["B"], a["Hq"], a["Hkv"], a["S"], a["d"],
+                                 a["P"], rank, t, a["causal"], a["layout"], a["dtype"], kv_splits, ws,
+                                 ws_bytes, NULL)
+
+    assert call(-1) == ra.RA_ERR_INVALID_ARG
+    assert call(65) == ra.RA_ERR_INVALID_ARG                     # above RA_MAX_KV_SPLITS
+    assert call(2) == ra.RA_ERR_INVALID_ARG                      # explicit splits, no workspace
+    need = ra.ra_fwd_workspace_bytes(1, 8, 8, 8192, 128, 8, False, True, "zigzag", 1, 2)
+    assert call(2, FAKE, need - 1) == ra.RA_ERR_INVALID_ARG      # one byte short
+    assert call(2, ctypes.c_void_p(0x1004), need) == ra.RA_ERR_INVALID_ARG
+    assert "aligned" in ra.last_error()
+    assert call(2, FAKE, -5) == ra.RA_ERR_INVALID_ARG
+    assert call(0, t=8) == ra.RA_ERR_INVALID_ARG
+    assert call(0, rank=-1) == ra.RA_ERR_INVALID_ARG
+    assert call(0, d=80) == ra.RA_ERR_UNSUPPORTED
+
+
+@cpu_only
 def test_round_robin_cache_rejects_before_the_device():
     L = ra.lib()
     # K_cache, V_cache, K_new, V_new, B, Hkv, d, P, cap, len, n_new, block, dtype

@@ -347,18 +347,28 @@ RING = [  # B, S, Hq, Hkv, d, P, layout, causal, dtype
 ]
 
 
-def _ring_rank(Qs, Ks, Vs, S, P, r, causal, layout, order=None):
-    """Run rank r's P steps, each on a copy of the arriving block only."""
+def _ring_rank(Qs, Ks, Vs, S, P, r, causal, layout, order=None, splits=None):
+    """Run rank r's P steps, each on a copy of the arriving block only
+    (through ra_ring_step_ws with ``splits`` key ranges when given)."""
     B, _, Hq, d = Qs.shape
+    Hkv = Ks.shape[2]
     n = S // P
     Qr = Qs[:, r * n:(r + 1) * n].contiguous()
     O = torch.empty(B, n, Hq, d, dtype=torch.float32, device="cuda")
     L = torch.empty(B, Hq, n, dtype=torch.float32, device="cuda")
+    ws = None
+    if splits is not None:
+        dt = ra.DTYPE_BF16 if Qs.dtype == torch.bfloat16 else ra.DTYPE_F32
+        nb = ra.ra_fwd_workspace_bytes(B, Hq, Hkv, S, d, P, False, causal, layout, dt, splits)
+        ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda") if nb > 0 else None
     for t in (order or range(P)):
         s = (r - t) % P
         Kb = Ks[:, s * n:(s + 1) * n].contiguous()
         Vb = Vs[:, s * n:(s + 1) * n].contiguous()
-        ra.ra_ring_step(Qr, Kb, Vb, O, L, S, P, r, t, causal, layout)
+        if splits is None:
+            ra.ra_ring_step(Qr, Kb, Vb, O, L, S, P, r, t, causal, layout)
+        else:
+            ra.ra_ring_step_ws(Qr, Kb, Vb, O, L, S, P, r, t, causal, layout, splits, ws)
     torch.cuda.synchronize()
     return O, L
 
@@ -393,6 +403,45 @@ def test_ring_step_fold(case):
     # t = 0 first, the rest reversed
     r = P - 1
     O2, L2 = _ring_rank(Qs, Ks, Vs, S, P, r, causal, layout, order=[0] + list(range(P - 1, 0, -1)))
+    assert (O2 - O_g[:, r * n:(r + 1) * n]).abs().max().item() <= tol
+    assert (L2 - L_g[:, :, r * n:(r + 1) * n]).abs().max().item() <= tol
+
+
+@pytest.mark.parametrize("case", [RING[0], RING[1], RING[2], RING[5]], ids=lambda c: _id(c))
+def test_ring_step_key_range_splits(case):
+    """ra_ring_step_ws: one range is ra_ring_step bit for bit; more ranges
+    (and the automatic choice) fold the ranges and the running state in one
+    merge and reach the oracle's result, in any order of the steps after
+    t = 0."""
+    B, S, Hq, Hkv, d, P, layout, causal, dtype = case
+    log(f"ring steps with splits {_id(case)}")
+    Qn, Kn, Vn = qkv(B, S, S, Hq, Hkv, d, dtype, (1350, S, P))
+    (Qs, Ks, Vs), _, _ = _run_prefill(Qn, Kn, Vn, P, layout, causal, dtype)
+    O_ref, lse_ref = oracle.attention(Qn, Kn, Vn, causal)
+    n = S // P
+    tol = BF16_O_MAX if dtype == "bf16" else F32_O_MAX
+    for r in range(P):
+        O1, L1 = _ring_rank(Qs, Ks, Vs, S, P, r, causal, layout)
+        Ow, Lw = _ring_rank(Qs, Ks, Vs, S, P, r, causal, layout, splits=1)
+        assert torch.equal(O1, Ow) and torch.equal(L1, Lw), f"rank {r}: one range differs"
+    for splits in (3, 0):
+        O_g = torch.empty(B, S, Hq, d, dtype=torch.float32, device="cuda")
+        L_g = torch.empty(B, Hq, S, dtype=torch.float32, device="cuda")
+        for r in range(P):
+            O, L = _ring_rank(Qs, Ks, Vs, S, P, r, causal, layout, splits=splits)
+            O_g[:, r * n:(r + 1) * n] = O
+            L_g[:, :, r * n:(r + 1) * n] = L
+            O1, L1 = _ring_rank(Qs, Ks, Vs, S, P, r, causal, layout)
+            assert (O - O1).abs().max().item() <= tol
+            fin = torch.isfinite(L1)
+            assert torch.equal(torch.isfinite(L), fin)
+            assert (L[fin] - L1[fin]).abs().max().item() <= tol
+        e = check(unshard(from_dev(O_g), S, P, layout, axis=1), O_ref,
+                  unshard(from_dev(L_g), S, P, layout, axis=2), lse_ref, dtype, f"{_id(case)} splits={splits}")
+        log(f"  splits={splits} ok {fmt(e)}")
+    # t = 0 first, the rest reversed
+    r = P - 1
+    O2, L2 = _ring_rank(Qs, Ks, Vs, S, P, r, causal, layout, order=[0] + list(range(P - 1, 0, -1)), splits=3)
     assert (O2 - O_g[:, r * n:(r + 1) * n]).abs().max().item() <= tol
     assert (L2 - L_g[:, :, r * n:(r + 1) * n]).abs().max().item() <= tol
 
