@@ -77,39 +77,174 @@ def measured_traffic(kernel: str, files, key: str = "bytes_per_launch"):
     return rec.get(key)
 
 
-def cpu_baseline(w, rank: int, n_rows: int):
-    """The fp64 oracle on a bounded sample of the prefill workload: n_rows
-    query rows of ``rank``, evenly spaced over its local rows (under the
-    zig-zag split half from each of its two chunks), every query head, each
-    row scored against all the keys it may see.  Returns TFLOP/s in the same
-    FLOP convention as the GPU figure."""
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return ""
+
+
+def _affinity_cores() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def _prefill_inputs_host(w):
+    from long_context_exact_amd import synthetic
+
+    dt = w.dtype
+    return (synthetic.normal_tensor(w.q_shape, w.seed(0), dt),
+            synthetic.normal_tensor(w.kv_shape, w.seed(1), dt),
+            synthetic.normal_tensor(w.kv_shape, w.seed(2), dt))
+
+
+def cpu_prefill(w, rank=None, n_rows=None):
+    """The fp64 oracle on a prefill workload: every row (rank None) or n_rows
+    query rows of ``rank`` evenly spaced over its local rows (under the
+    zig-zag split half from each of its two chunks); every query head, each
+    row scored against all the keys it may see.  Returns (seconds, FLOPs in
+    the GPU figure's convention, description)."""
+    import numpy as np
+
+    import oracle
+
+    Q, K, V = _prefill_inputs_host(w)
+    if rank is None:
+        rows = np.arange(w.S, dtype=np.int64)
+        what = f"all {w.S} rows"
+    else:
+        n = w.S // w.P
+        mine = oracle.natural_positions(w.S, w.P, w.layout)[rank * n:(rank + 1) * n]
+        rows = mine[np.linspace(0, n - 1, n_rows).astype(np.int64)]
+        what = f"{len(rows)} query rows of rank {rank} evenly spaced over its {w.layout} rows"
+    keys = rows + 1 if w.causal else np.full(rows.shape, w.S, dtype=np.int64)
+    flops = 4 * w.d * w.Hq * w.B * int(np.sum(keys))
+    t0 = time.perf_counter()
+    oracle.attention_rows(Q, K, V, w.causal, np.zeros_like(rows), rows)
+    dt = time.perf_counter() - t0
+    return dt, flops, f"{what}, all {w.Hq} heads"
+
+
+def cpu_decode_sequence(w, b: int = 0):
+    """The fp64 oracle on one whole sequence of the decode workload: its
+    query row of every head against all of its keys.  Returns (seconds,
+    algorithmic K/V bytes of that sequence, FLOPs)."""
     import numpy as np
 
     import oracle
     from long_context_exact_amd import synthetic
 
-    Q = synthetic.normal_tensor(w.q_shape, w.seed(0), "bf16")
-    K = synthetic.normal_tensor(w.kv_shape, w.seed(1), "bf16")
-    V = synthetic.normal_tensor(w.kv_shape, w.seed(2), "bf16")
-    n = w.S // w.P
-    mine = oracle.natural_positions(w.S, w.P, w.layout)[rank * n:(rank + 1) * n]
-    rows = mine[np.linspace(0, n - 1, n_rows).astype(np.int64)]
-    flops = 4 * w.d * w.Hq * int(np.sum(rows + 1))
+    per_seq = w.S * w.Hkv * w.d
+    Q = synthetic.normal_tensor(w.q_shape, w.seed(0), "bf16")[b:b + 1]
+    K = synthetic.normal_range(w.seed(1), b * per_seq, (b + 1) * per_seq, "bf16").reshape(1, w.S, w.Hkv, w.d)
+    V = synthetic.normal_range(w.seed(2), b * per_seq, (b + 1) * per_seq, "bf16").reshape(1, w.S, w.Hkv, w.d)
     t0 = time.perf_counter()
-    oracle.attention_rows(Q, K, V, True, np.zeros_like(rows), rows)
+    oracle.attention_rows(Q, K, V, False, np.zeros(w.Sq, np.int64), np.arange(w.Sq, dtype=np.int64))
     dt = time.perf_counter() - t0
-    model = ""
-    try:
-        for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                model = line.split(":", 1)[1].strip()
-                break
-    except OSError:
-        pass
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle", "cpu_model": model,
-            "sample": f"{len(rows)} query rows of rank {rank} evenly spaced over its {w.layout} "
-                      f"rows, all {w.Hq} heads, {flops / 1e9:.1f} GFLOP, {dt:.1f} s wall"}
+    return dt, 2 * per_seq * 2, 4 * w.d * w.Sq * w.Hq * w.S
+
+
+def cpu_baseline(wp, rank: int, n_rows: int, with_legs: bool = True):
+    """The oracle timed on this host's cores (every core of the affinity
+    mask), on bounded samples of the workloads.  ``value`` is the headline
+    prefill sample (n_rows rows of one rank's share of wp); ``legs`` adds the
+    small fp32 workload and the 8k-token workload whole, a 32k-token sample,
+    and one whole sequence of the decode workload."""
+    import oracle
+    from long_context_exact_amd.workloads import WORKLOADS
+
+    cores = _affinity_cores()
+    oracle.set_num_threads(cores)
+    dt, flops, what = cpu_prefill(wp, rank, n_rows)
+    out = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+           "affinity_cores": cores, "kind": "oracle", "cpu_model": _cpu_model(),
+           "sample": f"{what} of {wp.name}, {flops / 1e9:.1f} GFLOP, {dt:.1f} s wall"}
+    if not with_legs:
+        return out
+    legs = {}
+    for cfg, rank_, rows_ in ((1, None, None), (2, None, None), (3, 0, 512)):
+        w = WORKLOADS[cfg]
+        log(f"cpu baseline: oracle on {w.name}")
+        dt, flops, what = cpu_prefill(w, rank_, rows_)
+        legs[w.name] = {"s": dt, "gflop": flops / 1e9, "tflops": flops / dt / 1e12,
+                        "sample": what if rank_ is not None else "whole problem"}
+    wd = WORKLOADS[5]
+    log(f"cpu baseline: oracle on one sequence of {wd.name}")
+    dt, nbytes, flops = cpu_decode_sequence(wd, 0)
+    legs[wd.name] = {"s": dt, "gbs": nbytes / dt / 1e9, "tflops": flops / dt / 1e12,
+                     "sample": f"sequence 0 of {wd.B}: {wd.Hq} heads x {wd.S} keys, "
+                               f"{nbytes / 1e9:.2f} GB of K/V, {flops / 1e9:.1f} GFLOP"}
+    out["legs"] = legs
+    return out
+
+
+def time_prefill_ranks(ra, torch, w, steps: int, warmup: int, dev):
+    """Every rank's share of a prefill workload (ra_fwd_rank_ws with the
+    automatic key-range splits) and all ranks in one launch (ra_fwd_all_ws),
+    timed with HIP events on the current stream.  The maximum over ranks is
+    how long one ring pass takes when the ranks run side by side."""
+    from long_context_exact_amd import synthetic
+    from long_context_exact_amd.workloads import prefill_flops
+
+    dt = ra.DTYPE_BF16 if w.dtype == "bf16" else ra.DTYPE_F32
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    nat = [synthetic.to_device(sh, w.seed(i), w.dtype, dev)
+           for i, sh in ((0, w.q_shape), (1, w.kv_shape), (2, w.kv_shape))]
+    Qs, Ks, Vs = (torch.empty_like(x) for x in nat)
+    for a, b in zip(nat, (Qs, Ks, Vs)):
+        ra.ra_layout_gather(a, b, w.S, w.P, w.layout, inverse=False)
+    del nat
+    n = w.S // w.P
+    O_r = torch.empty(w.B, n, w.Hq, w.d, dtype=torch.float32, device=dev)
+    L_r = torch.empty(w.B, w.Hq, n, dtype=torch.float32, device=dev)
+    ws_r_bytes = ra.ra_fwd_workspace_bytes(w.B, w.Hq, w.Hkv, w.S, w.d, w.P, False, w.causal,
+                                           w.layout, dt, 0)
+    ws_r = torch.empty(max(ws_r_bytes, 1), dtype=torch.uint8, device=dev)
+
+    def timed(fn, k):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(k):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / k
+
+    per = []
+    for r in range(w.P):
+        Qr = Qs[:, r * n:(r + 1) * n]
+        per.append(timed(lambda: ra.ra_fwd_rank_ws(Qr, Ks, Vs, O_r, L_r, w.P, r, w.causal, w.layout,
+                                                   0, ws_r), steps))
+    O_all = torch.empty(w.B, w.S, w.Hq, w.d, dtype=torch.float32, device=dev)
+    L_all = torch.empty(w.B, w.Hq, w.S, dtype=torch.float32, device=dev)
+    ws_a_bytes = ra.ra_fwd_workspace_bytes(w.B, w.Hq, w.Hkv, w.S, w.d, w.P, True, w.causal,
+                                           w.layout, dt, 0)
+    ws_a = torch.empty(max(ws_a_bytes, 1), dtype=torch.uint8, device=dev)
+    all_ms = timed(lambda: ra.ra_fwd_all_ws(Qs, Ks, Vs, O_all, L_all, w.P, w.causal, w.layout, 0, ws_a),
+                   steps)
+    total = prefill_flops(w)
+    rank_flops = [prefill_flops(w, r) for r in range(w.P)]
+    return {"workload": w.name, "layout": w.layout,
+            "rank_ms": [round(x, 4) for x in per],
+            "rank_gflop": [round(f / 1e9, 2) for f in rank_flops],
+            "rank_tflops": [round(f / (t * 1e-3) / 1e12, 1) for f, t in zip(rank_flops, per)],
+            "slowest_rank_ms": max(per), "max_over_min": max(per) / min(per),
+            "sum_of_ranks_ms": sum(per),
+            "tflops_per_gpu_at_slowest_rank": total / w.P / (max(per) * 1e-3) / 1e12,
+            "all_ranks_one_launch_ms": all_ms,
+            "all_ranks_tflops": total / (all_ms * 1e-3) / 1e12,
+            "all_ranks_frac_bf16_peak": total / (all_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "gflop_total": total / 1e9,
+            "kv_splits_rank": (ws_r_bytes // (w.B * n * w.Hq * (w.d + 1) * 4)) if ws_r_bytes else 1,
+            "kv_splits_all": (ws_a_bytes // (w.B * w.S * w.Hq * (w.d + 1) * 4)) if ws_a_bytes else 1}
 
 
 def sample_sclk(fn, seconds: float = 3.0):
@@ -161,7 +296,11 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--rank", type=int, default=0, help="prefill rank whose share is timed")
     ap.add_argument("--decode-parts", type=int, default=64)
-    ap.add_argument("--cpu-rows", type=int, default=128)
+    ap.add_argument("--cpu-rows", type=int, default=256,
+                    help="query rows of the timed rank in the CPU oracle's headline sample")
+    ap.add_argument("--no-other-prefill", action="store_true",
+                    help="skip timing every rank and the all-ranks launch of the 8k and 32k-token "
+                         "prefill workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill-cfg", type=int, choices=[2, 3, 4], default=4,
                     help="prefill workload: 4 = 128k-token GQA (default, the headline), 3 = 32k "
@@ -599,9 +738,18 @@ def main() -> int:
             "note": "one GPU: the all-to-all is a local transposition; the ring's block exchange is "
                     "not simulated (all shards resident)"}
         del Qh, Kh, Vh, Oh, Lh, O_n, L_n, O_all, L_all, wsu, wsr
+    if do_pre and not args.no_other_prefill and args.prefill_cfg == 4 and args.layout is None:
+        # the 8k-token naive split and the 32k-token zig-zag split: per-rank
+        # balance and the all-ranks time (parity-tested workloads, not the headline)
+        out["other_prefill"] = {}
+        for c in (2, 3):
+            log(f"timing every rank of {WORKLOADS[c].name}")
+            out["other_prefill"][f"cfg{c}"] = time_prefill_ranks(ra, torch, WORKLOADS[c], args.steps,
+                                                                 args.warmup, dev)
     if do_pre and not args.no_cpu_baseline:
-        log(f"cpu baseline: oracle on {args.cpu_rows} sampled rows")
-        out["cpu_baseline"] = cpu_baseline(wp, args.rank, args.cpu_rows)
+        log(f"cpu baseline: oracle on {args.cpu_rows} sampled rows and the other workloads' samples")
+        out["cpu_baseline"] = cpu_baseline(wp, args.rank, args.cpu_rows,
+                                           with_legs=args.prefill_cfg == 4 and args.layout is None)
     print(json.dumps(out), flush=True)
     return 0
 

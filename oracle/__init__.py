@@ -227,12 +227,19 @@ def _load():
         lib.oracle_merge.argtypes = [vp, vp, i64, i64, i64, vp, vp]
         lib.oracle_merge.restype = ctypes.c_int
         lib.oracle_num_threads.restype = ctypes.c_int
+        lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
+        lib.oracle_set_num_threads.restype = None
         _lib = lib
     return _lib
 
 
 def num_threads() -> int:
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads the C oracle's parallel regions use from now on."""
+    _load().oracle_set_num_threads(int(n))
 
 
 def _elem(a: np.ndarray) -> int:

@@ -92,14 +92,15 @@ def check(O, O_ref, lse, lse_ref, dtype: str, what: str = "", o_rounded: bool = 
 
 def sample_rows(S: int, P: int, layout: str, per_rank: int, seed) -> np.ndarray:
     """Natural positions to check: per rank the first and last row of each of
-    its chunks plus ``per_rank`` rows drawn with a seeded generator."""
-    rng = np.random.default_rng(seed)
+    its chunks plus ``per_rank`` rows drawn with the seeded generator
+    ``numpy.random.default_rng([*seed, rank])``."""
     pos = oracle.natural_positions(S, P, layout)
     n = S // P
     # a striped rank's rows are one strided chunk
     c = n if layout == "striped" else oracle.chunk_len(layout, S, P)
     rows = []
     for r in range(P):
+        rng = np.random.default_rng([*seed, r])
         mine = pos[r * n:(r + 1) * n]
         for k in range(0, n, c):
             rows += [mine[k], mine[k + c - 1]]

@@ -3,8 +3,9 @@ configuration the benchmark times.
 
 Small workloads are checked on every output row; the 32k and 128k-token
 workloads on seeded sampled rows (per rank: the first and last row of each
-of its chunks plus random rows), every query head; the 1M-key decode on two
-whole sequences (all 64 heads)."""
+of its chunks plus 60 rows drawn with numpy.random.default_rng([cfg, 3,
+rank])), every query head; the 1M-key decode on all 8 of its sequences, every
+head (one query row per sequence and head)."""
 import dataclasses
 
 import numpy as np
@@ -18,6 +19,8 @@ from long_context_exact_amd import synthetic
 from long_context_exact_amd.workloads import WORKLOADS
 
 pytestmark = pytest.mark.gpu
+
+ROWS_PER_RANK = 60  # drawn rows per rank of the sampled workloads (besides chunk ends)
 
 
 def _inputs(w):
@@ -81,11 +84,28 @@ def test_prefill_workload(cfg, layout):
         O_ref, L_ref = oracle.attention(Qn, Kn, Vn, w.causal)
         e = check(O_h, O_ref, L_h, L_ref, w.dtype, w.name)
     else:
-        rows = sample_rows(S, P, lay, 16 if cfg == 3 else 12, [cfg, 3])
+        rows = sample_rows(S, P, lay, ROWS_PER_RANK, [cfg, 3])
         log(f"workload {cfg}: oracle on {len(rows)} sampled rows")
         O_ref, L_ref = oracle.attention_rows(Qn, Kn, Vn, w.causal, np.zeros_like(rows), rows)
         e = check(O_h[0, rows], O_ref, L_h[0][:, rows].T, L_ref, w.dtype, w.name)
     log(f"workload {cfg}: ok {fmt(e)}")
+
+
+def _check_decode_sequences(w, qh, O_g, L_g, what):
+    """Every sequence of the decode workload against the oracle: its query
+    row of every head over all of its keys.  Each sequence's K/V are
+    regenerated on the host from the same seeded ranges."""
+    per_seq = w.S * w.Hkv * w.d
+    for b in range(w.B):
+        log(f"workload 5 {what}: oracle on sequence {b}")
+        Kb = synthetic.normal_range(w.seed(1), b * per_seq, (b + 1) * per_seq, "bf16")
+        Vb = synthetic.normal_range(w.seed(2), b * per_seq, (b + 1) * per_seq, "bf16")
+        Kb = Kb.reshape(1, w.S, w.Hkv, w.d)
+        Vb = Vb.reshape(1, w.S, w.Hkv, w.d)
+        O_ref, L_ref = oracle.attention_rows(qh[b:b + 1], Kb, Vb, False, [0], [0])
+        e = check(O_g[b][None], O_ref, L_g[b][None], L_ref, "bf16", f"{what} sequence {b}")
+        log(f"workload 5 {what} sequence {b}: ok {fmt(e)}")
+        del Kb, Vb
 
 
 def test_decode_workload():
@@ -126,22 +146,13 @@ def test_decode_workload():
     qh = Q.cpu().view(torch.int16).numpy().view(np.uint16)
     del K, V, Op, lp, shard_O, shard_l
     torch.cuda.empty_cache()
-    per_seq = w.S * w.Hkv * w.d
-    for b in (0, w.B - 1):
-        log(f"workload 5: oracle on sequence {b}")
-        Kb = synthetic.normal_range(w.seed(1), b * per_seq, (b + 1) * per_seq, "bf16")
-        Vb = synthetic.normal_range(w.seed(2), b * per_seq, (b + 1) * per_seq, "bf16")
-        Kb = Kb.reshape(1, w.S, w.Hkv, w.d)
-        Vb = Vb.reshape(1, w.S, w.Hkv, w.d)
-        O_ref, L_ref = oracle.attention_rows(qh[b:b + 1], Kb, Vb, False, [0], [0])
-        e = check(O_g[b][None], O_ref, L_g[b][None], L_ref, "bf16", f"sequence {b}")
-        log(f"workload 5 sequence {b}: ok {fmt(e)}")
+    _check_decode_sequences(w, qh, O_g, L_g, "contiguous cache")
 
 
 def test_decode_workload_round_robin_cache():
     """The 1M-key decode workload with its cache dealt round-robin in blocks
     of 64 tokens over the 8 shards (built by ra_kv_append_rr), 8 parts per
-    shard, merged; checked against the oracle on two whole sequences."""
+    shard, merged; checked against the oracle on all 8 sequences."""
     w = WORKLOADS[5]
     block, pps = 64, 8
     log(f"workload 5 {w.name}: round-robin cache, blocks of {block}")
@@ -173,13 +184,4 @@ def test_decode_workload_round_robin_cache():
     qh = Q.cpu().view(torch.int16).numpy().view(np.uint16)
     del Kc, Vc, Op, lp
     torch.cuda.empty_cache()
-    per_seq = w.S * w.Hkv * w.d
-    for b in (0, w.B - 1):
-        log(f"workload 5 round-robin: oracle on sequence {b}")
-        Kb = synthetic.normal_range(w.seed(1), b * per_seq, (b + 1) * per_seq, "bf16")
-        Vb = synthetic.normal_range(w.seed(2), b * per_seq, (b + 1) * per_seq, "bf16")
-        Kb = Kb.reshape(1, w.S, w.Hkv, w.d)
-        Vb = Vb.reshape(1, w.S, w.Hkv, w.d)
-        O_ref, L_ref = oracle.attention_rows(qh[b:b + 1], Kb, Vb, False, [0], [0])
-        e = check(O_g[b][None], O_ref, L_g[b][None], L_ref, "bf16", f"round-robin sequence {b}")
-        log(f"workload 5 round-robin sequence {b}: ok {fmt(e)}")
+    _check_decode_sequences(w, qh, O_g, L_g, "round-robin cache")

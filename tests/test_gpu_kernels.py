@@ -446,6 +446,51 @@ def test_ring_step_key_range_splits(case):
     assert (L2 - L_g[:, :, r * n:(r + 1) * n]).abs().max().item() <= tol
 
 
+def test_ring_step_automatic_and_many_ranges():
+    """The automatic range count of a ring step on a block of 2048 keys is
+    two (at most one range per 1024 keys of the block): its result differs
+    from one range and equals an explicit kv_splits = 2 bit for bit, and
+    every rank reaches the oracle.  Twelve explicit ranges take the merge's
+    path for more than eight parts, which folds the running state as its
+    first part; most of those ranges are empty on this small block."""
+    B, S, Hq, Hkv, d, P, layout, causal, dtype = 1, 16384, 2, 2, 128, 8, "zigzag", True, "bf16"
+    log("ring steps, automatic ranges on 2048-key blocks")
+    Qn, Kn, Vn = qkv(B, S, S, Hq, Hkv, d, dtype, (1360, S, P))
+    Qs, Ks, Vs = (to_dev(shard(x, S, P, layout)) for x in (Qn, Kn, Vn))
+    O_ref, lse_ref = oracle.attention(Qn, Kn, Vn, causal)
+    n = S // P
+    O_g = torch.empty(B, S, Hq, d, dtype=torch.float32, device="cuda")
+    L_g = torch.empty(B, Hq, S, dtype=torch.float32, device="cuda")
+    for r in range(P):
+        O0, L0 = _ring_rank(Qs, Ks, Vs, S, P, r, causal, layout, splits=0)
+        O2, L2 = _ring_rank(Qs, Ks, Vs, S, P, r, causal, layout, splits=2)
+        O1, L1 = _ring_rank(Qs, Ks, Vs, S, P, r, causal, layout)
+        assert torch.equal(O0, O2) and torch.equal(L0, L2), f"rank {r}: automatic != 2 ranges"
+        assert not torch.equal(O0, O1), f"rank {r}: automatic choice ran one range"
+        O_g[:, r * n:(r + 1) * n] = O0
+        L_g[:, :, r * n:(r + 1) * n] = L0
+    e = check(unshard(from_dev(O_g), S, P, layout, axis=1), O_ref,
+              unshard(from_dev(L_g), S, P, layout, axis=2), lse_ref, dtype, "automatic ranges")
+    log(f"  automatic (2 ranges) ok {fmt(e)}")
+
+    B, S, Hq, Hkv, d, P, layout, causal, dtype = RING[0]
+    log(f"ring steps with 12 ranges {_id(RING[0])}")
+    Qn, Kn, Vn = qkv(B, S, S, Hq, Hkv, d, dtype, (1370, S, P))
+    Qs, Ks, Vs = (to_dev(shard(x, S, P, layout)) for x in (Qn, Kn, Vn))
+    O_ref, lse_ref = oracle.attention(Qn, Kn, Vn, causal)
+    n = S // P
+    O_g = torch.empty(B, S, Hq, d, dtype=torch.float32, device="cuda")
+    L_g = torch.empty(B, Hq, S, dtype=torch.float32, device="cuda")
+    for r in range(P):
+        order = [0] + list(range(P - 1, 0, -1)) if r % 2 else None
+        O, L = _ring_rank(Qs, Ks, Vs, S, P, r, causal, layout, order=order, splits=12)
+        O_g[:, r * n:(r + 1) * n] = O
+        L_g[:, :, r * n:(r + 1) * n] = L
+    e = check(unshard(from_dev(O_g), S, P, layout, axis=1), O_ref,
+              unshard(from_dev(L_g), S, P, layout, axis=2), lse_ref, dtype, "12 ranges")
+    log(f"  12 ranges ok {fmt(e)}")
+
+
 def test_ring_step_double_buffered_streams():
     """The schedule a multi-GPU ring would run: while step t computes on one
     receive buffer, the next block is copied into the other on a second
