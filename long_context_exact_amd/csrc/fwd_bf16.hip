@@ -37,9 +37,10 @@
 // O += V_{i-1} P_{i-1} and, in between them, the softmax of S_i.  The stage
 // opens with a PV product whose V operand was read before the barrier, so an
 // MFMA is in flight while the K operands arrive and the next loads go out.
-// K/V tiles go from global memory straight into a ring of four LDS buffers
-// (global_load_lds_dwordx4, no staging registers), two tiles ahead of the tile
-// whose scores are being formed.  The loop body is unrolled over the ring so
+// K/V tiles go from global memory straight into rings of four LDS buffers
+// (global_load_lds_dwordx4, no staging registers): stage i loads K of tile i+3
+// and V of tile i+2, two stages before their use, and waits only for the loads
+// of two stages before.  The loop body is unrolled over the ring so
 // that every LDS operand address is a per-lane base plus an immediate offset.
 #include <type_traits>
 
@@ -139,25 +140,31 @@ struct KvTile {
     }
     // Rows at or past klen (the ragged end of a chunk) repeat row 0: finite
     // data under keys that the mask removes.
-    static __device__ __forceinline__ void load(const uint16_t* Kb, const uint16_t* Vb, const Offs& o,
-                                                int klen, uint32_t row_bytes, const uint16_t* Ks,
+    // Load q of a K/V tile pair: q < ROUNDS is round q of K, the rest the
+    // rounds of V (so a stage can spread its loads between its MFMAs).  The K
+    // and the V tile of one load set belong to different key tiles.  Only a
+    // launch whose chunk length is not a multiple of BN (RAGGED) has tiles
+    // with fewer than BN rows.
+    template <bool RAGGED>
+    static __device__ __forceinline__ void load_one(int q, const uint16_t* Kb, int klen, const uint16_t* Vb,
+                                                    int vlen, const Offs& o, uint32_t row_bytes,
+                                                    const uint16_t* Ks, const uint16_t* Vs, int w, int lane) {
+        const bool is_v = q >= ROUNDS;
+        const int r = is_v ? q - ROUNDS : q;
+        const uint16_t* g = is_v ? Vb : Kb;
+        const int len = is_v ? vlen : klen;
+        const uint32_t lds = lds_addr((is_v ? Vs : Ks) + (NT * r + 64 * w) * 8);
+        if (!RAGGED || len >= BN)
+            lds_dma16(g + (int64_t)r * ROWS_PER_ROUND * (row_bytes / 2), is_v ? o.v : o.k, lds);
+        else
+            lds_dma16(g, chunk_off(r, w, lane, len, row_bytes, is_v), lds);
+    }
+    template <bool RAGGED>
+    static __device__ __forceinline__ void load(const uint16_t* Kb, int klen, const uint16_t* Vb, int vlen,
+                                                const Offs& o, uint32_t row_bytes, const uint16_t* Ks,
                                                 const uint16_t* Vs, int w, int lane) {
-        if (klen >= BN) {
 #pragma unroll
-            for (int r = 0; r < ROUNDS; ++r) {
-                const int64_t ro = (int64_t)r * ROWS_PER_ROUND * (row_bytes / 2);
-                lds_dma16(Kb + ro, o.k, lds_addr(Ks + (NT * r + 64 * w) * 8));
-                lds_dma16(Vb + ro, o.v, lds_addr(Vs + (NT * r + 64 * w) * 8));
-            }
-        } else {
-#pragma unroll
-            for (int r = 0; r < ROUNDS; ++r) {
-                lds_dma16(Kb, chunk_off(r, w, lane, klen, row_bytes, false),
-                          lds_addr(Ks + (NT * r + 64 * w) * 8));
-                lds_dma16(Vb, chunk_off(r, w, lane, klen, row_bytes, true),
-                          lds_addr(Vs + (NT * r + 64 * w) * 8));
-            }
-        }
+        for (int q = 0; q < LOADS; ++q) load_one<RAGGED>(q, Kb, klen, Vb, vlen, o, row_bytes, Ks, Vs, w, lane);
     }
 };
 
@@ -256,6 +263,22 @@ __device__ __forceinline__ int cur_count(const FwdParams& p, int rank, int qmax)
     return n;
 }
 
+// The loader's cursor: cur_next that also moves the tile's K row pointer, by
+// one tile inside a segment and from the segment's first row after a jump.
+__device__ __forceinline__ void lc_next(const FwdParams& p, int rank, int qmax, KvCur& c, const uint16_t*& kp,
+                                        const uint16_t* Kg, int64_t row_stride) {
+    if (c.tl > 0) {
+        --c.tl;
+        c.krow += BN;
+        c.kpos += BN;
+        c.cleft -= BN;
+        kp += BN * row_stride;
+    } else {
+        cur_skip(p, rank, qmax, c);
+        kp = Kg + c.krow * row_stride;
+    }
+}
+
 // Masks keys of a tile outside the query's causal window or past a ragged
 // chunk end.  Register r of block kb2 holds key kb2*32 + 16*(r/8) + 8h + r%8.
 __device__ __forceinline__ void mask_tile(f32x16 (&s)[2], int lim) {
@@ -290,7 +313,7 @@ __device__ __forceinline__ void exp_tile(const f32x16 (&s)[2], float c, float mu
         }
 }
 
-template <int D>
+template <int D, bool RAGGED>
 __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdParams p) {
     using T = KvTile<D>;
     constexpr int KB = D / 16;    // MFMA k-blocks of Q K^T
@@ -348,27 +371,48 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdParams p) {
     const uint16_t* Vg = (const uint16_t*)p.V + ((int64_t)qt.b * p.kv_rows * p.Hkv + qt.kvh) * D;
     const typename T::Offs offs = T::offsets(w, lane, row_bytes);
 
-    // ---- prologue: tiles 0 and 1 on their way into buffers 0 and 1; the V
-    // buffer "before" tile 0 zeroed (the first PV product multiplies P = 0)
-    // this work-group's key range: tiles [i0, i1) of the tile's visiting order
+    // ---- prologue.  Stage i issues the loads of K of tile i+3 and V of tile
+    // i+2 (two stages before their use), so K of tiles 0-2 and V of tiles 0-1
+    // go out here; the V buffer "before" tile 0 is zeroed (the first PV
+    // product multiplies P = 0).  Past the work-group's last tile the loads
+    // repeat that tile into buffers that no later stage reads, so every stage
+    // issues the same number of loads and one wait count fits all stages.
+    // This work-group's key range: tiles [i0, i0 + n) of the tile's visiting order.
     const int n_all = cur_count(p, qt.rank, qmax);
     const int i0 = (int)(((int64_t)n_all * split) / p.kv_splits);
     const int n = (int)(((int64_t)n_all * (split + 1)) / p.kv_splits) - i0;
-    KvCur it_c, it_l;  // tile i of the loop; last tile whose loads were issued
-    int issued = 0;    // tiles whose loads were issued
+    KvCur it_c, it_l;            // tile i of the loop; the K loader's tile
+    const uint16_t* kp_l = Kg;   // K rows of the K loader's tile
+    int klen_l = BN;             // rows of that tile inside its chunk
+    int64_t voff_l = 0;          // K/V element offset of the V loader's tile (one behind)
+    int vlen_l = BN;
+    int issued = 0;              // tiles up to and including the K loader's
+    // K loader to the next tile (it stays on the last one)
+    auto advance_loader = [&]() {
+        if (issued < n) {
+            lc_next(p, qt.rank, qmax, it_l, kp_l, Kg, row_stride);
+            if (RAGGED) klen_l = min(it_l.cleft, BN);
+            ++issued;
+        }
+    };
     if (n > 0) {
         cur_first(p, qt.rank, qmax, it_c);
         cur_advance(p, qt.rank, qmax, it_c, i0);
         it_l = it_c;
-        T::load(Kg + it_l.krow * row_stride, Vg + it_l.krow * row_stride, offs, min(it_l.cleft, BN),
-                row_bytes, ldsK[0], ldsV[0], w, lane);
+        kp_l = Kg + it_l.krow * row_stride;
+        klen_l = min(it_l.cleft, BN);
         issued = 1;
-        for (int j = 1; j < 2 && j < n; ++j) {
-            cur_next(p, qt.rank, qmax, it_l);
-            T::load(Kg + it_l.krow * row_stride, Vg + it_l.krow * row_stride, offs, min(it_l.cleft, BN),
-                    row_bytes, ldsK[j], ldsV[j], w, lane);
-            issued = j + 1;
-        }
+        T::template load<RAGGED>(kp_l, klen_l, Vg + (kp_l - Kg), klen_l, offs, row_bytes, ldsK[0], ldsV[0], w, lane);
+        advance_loader();
+        T::template load<RAGGED>(kp_l, klen_l, Vg + (kp_l - Kg), klen_l, offs, row_bytes, ldsK[1], ldsV[1], w, lane);
+        advance_loader();
+#pragma unroll
+        for (int q = 0; q < T::ROUNDS; ++q)
+            T::template load_one<RAGGED>(q, kp_l, klen_l, Vg, BN, offs, row_bytes, ldsK[2], ldsV[2], w, lane);
+        // stage 0 loads V of tile 2 (the loader's tile now) and K of tile 3
+        voff_l = kp_l - Kg;
+        vlen_l = klen_l;
+        advance_loader();
     }
     for (int e = t * 8; e < T::ELEMS; e += NT * 8)
         *(uint4*)(&ldsV[NBUF - 1][e]) = make_uint4(0, 0, 0, 0);
@@ -376,7 +420,8 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdParams p) {
     // LDS operand addresses.  Both chunk swizzles are XORs into address bits
     // that the row part leaves clear, so the byte address of an operand is
     // (per-lane base) ^ (constant of its dim block) + (constant of its row
-    // block and buffer): one base register per tensor and one v_xor per read.
+    // block and buffer): twelve XORed bases (eight for K, four for V) and an
+    // immediate offset per read.
     //
     // K operand j: keys 32*(j%2).. (rows permuted), dims 16*(j/2)..: the two
     // S^T accumulators alternate, so consecutive MFMAs are independent.  Lane
@@ -406,13 +451,12 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdParams p) {
         return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
 
-    // tile 0 resident (tile 1 may be in flight); its scores
+    // scores of tile 0
     f32x16 sa[2], sb[2];  // S of tiles i and i+1 (roles swap every iteration)
     bf16x8 pa[4], pb[4];  // P of tiles i-1 and i (roles swap every iteration)
-    if (issued > 1)
-        __builtin_amdgcn_s_waitcnt(0x0F70 | T::LOADS);
-    else
-        __builtin_amdgcn_s_waitcnt(0x0F70);
+    // K of tile 0 resident: the V of tiles 0-1 and K of tiles 1-2 may still fly
+    static_assert(2 * T::LOADS < 16, "wait count fits the vmcnt field");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * T::LOADS));
     __syncthreads();
     // V operand 0 of the next stage's first MFMA (a PV product), read before
     // the barrier that opens the stage: V of tile i-1 has long been resident
@@ -434,14 +478,16 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdParams p) {
     auto iteration = [&](auto slot, int i, f32x16 (&sc)[2], f32x16 (&sn)[2], bf16x8 (&pp)[4],
                          bf16x8 (&pc)[4]) {
         constexpr int SLOT = decltype(slot)::value;
-        // tile i+1 resident; the buffer of tile i-2 is free for tile i+2
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        // K of tile i+1 resident (the loads of the previous stage may still
+        // fly); after the barrier the K buffer of tile i-1 and the V buffer of
+        // tile i-2 are free for K of tile i+3 and V of tile i+2
+        __builtin_amdgcn_s_waitcnt(0x0F70 | T::LOADS);
         __syncthreads();
         // S_{i+1} from buffer (i+1) (stale data past the last tile: unused)
         constexpr int KBUF = (SLOT + 1) % NBUF, VBUF = (SLOT + NBUF - 1) % NBUF;
 
-        const int klen = min(it_c.cleft, BN);
-        if (klen < BN || (p.causal && it_c.kpos + BN - 1 > wq_lo)) {
+        const int klen = RAGGED ? min(it_c.cleft, BN) : BN;
+        if ((RAGGED && klen < BN) || (p.causal && it_c.kpos + BN - 1 > wq_lo)) {
             const int lim = p.causal ? min(max(qpos - it_c.kpos + 1, 0), klen) : klen;
             mask_tile(sc, lim - 8 * h);
         }
@@ -453,9 +499,9 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdParams p) {
         // temporaries are live.  sched_barrier keeps this order.
         float lsum = 0.f, lrsum = 0.f;
         {
-            // recompute the operand addresses in every stage rather than hold
-            // twelve of them in registers
-            asm volatile("" : "+v"(kbase), "+v"(vbase));
+            // The twelve operand addresses stay in registers; the kernel for
+            // ragged chunks, short of registers, recomputes them in every stage.
+            if (RAGGED) asm volatile("" : "+v"(kbase), "+v"(vbase));
             const float mu = m_ref;
             const bf16x2 kOnes = {(__bf16)1.0f, (__bf16)1.0f};
             constexpr int NE = 32;            // softmax elements per lane and tile
@@ -481,13 +527,15 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdParams p) {
                     else
                         oacc[q % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pp[q / DB], oacc[q % DB], 0, 0, 0);
                     if (j >= 1 && j + AHEAD < NMF) ops[j % AHEAD] = read_op(j + AHEAD);
-                    // the next tile's loads go out behind the first MFMA
-                    if (j == 0 && issued < n) {
-                        cur_next(p, qt.rank, qmax, it_l);
-                        T::load(Kg + it_l.krow * row_stride, Vg + it_l.krow * row_stride, offs, min(it_l.cleft, BN),
-                                row_bytes, ldsK[(SLOT + 2) % NBUF], ldsV[(SLOT + 2) % NBUF], w, lane);
-                        ++issued;
-                    }
+                    // The loads of tile i+2 (the loader cursor moved there at
+                    // the end of the previous stage): one behind each even
+                    // slot from the second on, so that their scalar work is
+                    // spread over the stage.  Past the last tile they repeat
+                    // the last tile into the buffer of tile i+2, which no later
+                    // stage reads.
+                    if (j >= 2 && (j & 1) == 0 && (j - 2) / 2 < T::LOADS)
+                        T::template load_one<RAGGED>((j - 2) / 2, kp_l, klen_l, Vg + voff_l, vlen_l, offs, row_bytes,
+                                                     ldsK[(SLOT + 3) % NBUF], ldsV[(SLOT + 2) % NBUF], w, lane);
                 }
 #pragma unroll
                 for (int q = 0; q < EPS; ++q) {
@@ -533,6 +581,11 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdParams p) {
         l_run += lsum;
         lr_run += lrsum;
         if (i + 1 < n) cur_next(p, qt.rank, qmax, it_c);
+        // the next stage loads V of the K loader's tile and K of the one
+        // after; this scalar work overlaps the stage's last MFMAs
+        voff_l = kp_l - Kg;
+        vlen_l = klen_l;
+        advance_loader();
         vpre = read_v(0, SLOT);
     };
 
@@ -543,6 +596,8 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdParams p) {
         if (i + 2 < n) iteration(std::integral_constant<int, 2>(), i + 2, sa, sb, pa, pb);
         if (i + 3 < n) iteration(std::integral_constant<int, 3>(), i + 3, sb, sa, pb, pa);
     }
+    // no load may still be writing LDS when the work-group ends
+    __builtin_amdgcn_s_waitcnt(0x0F70);
     if (n > 0 && (n - 1) % 2 == 0) {
         // the last tile's P is in the second copy: move it to the first
 #pragma unroll
@@ -620,10 +675,19 @@ hipError_t launch_fwd_bf16(const FwdParams& p, int d, hipStream_t s) {
     const int64_t tiles = (int64_t)p.n_ranks * p.chunks_per_rank * p.tiles_per_chunk;
     const int64_t grid = tiles * p.B * p.Hq * p.kv_splits;
     if (grid <= 0) return hipSuccess;
-    if (d == 128)
-        hipLaunchKernelGGL(fwd_bf16_kernel<128>, dim3((unsigned)grid), dim3(NT), 0, s, p);
-    else
-        hipLaunchKernelGGL(fwd_bf16_kernel<64>, dim3((unsigned)grid), dim3(NT), 0, s, p);
+    // chunks of a multiple of BN rows have no ragged key tile
+    const bool ragged = p.c % BN != 0;
+    if (d == 128) {
+        if (ragged)
+            hipLaunchKernelGGL((fwd_bf16_kernel<128, true>), dim3((unsigned)grid), dim3(NT), 0, s, p);
+        else
+            hipLaunchKernelGGL((fwd_bf16_kernel<128, false>), dim3((unsigned)grid), dim3(NT), 0, s, p);
+    } else {
+        if (ragged)
+            hipLaunchKernelGGL((fwd_bf16_kernel<64, true>), dim3((unsigned)grid), dim3(NT), 0, s, p);
+        else
+            hipLaunchKernelGGL((fwd_bf16_kernel<64, false>), dim3((unsigned)grid), dim3(NT), 0, s, p);
+    }
     return hipGetLastError();
 }
 
