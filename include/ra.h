@@ -47,7 +47,8 @@
  *     the device.  ra_last_error() gives a message for the calling thread's
  *     last failure.
  *   - Calls are re-entrant; the only global state is the thread-local error
- *     message.
+ *     message and the device scratch of ra_fwd_rank_noalloc (its calls on one
+ *     GPU share that scratch).
  */
 #ifndef RA_H
 #define RA_H
@@ -159,6 +160,34 @@ int ra_fwd_all_ws(const void* Q, const void* K, const void* V, void* O, float* L
                   int B, int Hq, int Hkv, int64_t S, int d, int P,
                   int causal, int layout, int dtype, int o_dtype,
                   int kv_splits, void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * ra_fwd_rank_noalloc -- ra_fwd_rank_ws for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  The key-range partials go to a scratch array that
+ * the library holds in device memory, RA_SCRATCH_BYTES per GPU it runs on,
+ * from the first call on that GPU until the process ends; the call itself
+ * makes no hipMalloc, hipFree or other allocating call.  The caller still
+ * passes the inputs and outputs.
+ *   kv_splits: 0 = automatic (as ra_fwd_rank_ws with a workspace of
+ *              RA_SCRATCH_BYTES: fewer ranges where their partials would not
+ *              fit); 1..RA_MAX_KV_SPLITS = exactly that many, and
+ *              RA_ERR_INVALID_ARG (before any HIP call) when their partials,
+ *              ra_fwd_workspace_bytes(..., all_ranks = 0, ..., kv_splits),
+ *              exceed RA_SCRATCH_BYTES.
+ * The result equals ra_fwd_rank_ws with the same kv_splits (and, in automatic
+ * mode, a workspace of RA_SCRATCH_BYTES) bit for bit.  Every call on one GPU
+ * shares that GPU's scratch: calls that overlap in time on one GPU (other
+ * streams, other threads) race and must be ordered by the caller.  The
+ * scratch's contents on entry do not matter; every range rewrites its
+ * partials.  All other arguments and requirements are those of ra_fwd_rank.
+ */
+#define RA_SCRATCH_BYTES ((int64_t)64 << 20)
+
+int ra_fwd_rank_noalloc(const void* Q_r, const void* K, const void* V, void* O_r, float* LSE_r,
+                        int B, int Hq, int Hkv, int64_t S, int d, int P, int rank,
+                        int causal, int layout, int dtype, int o_dtype, int kv_splits,
+                        void* stream);
 
 /*
  * ra_ring_step -- one step of the ring loop of one rank ([L8] section 2),

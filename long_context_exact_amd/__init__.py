@@ -28,6 +28,7 @@ def layout_zigzag_k(k: int) -> int:
 DTYPE_F32, DTYPE_BF16 = 0, 1
 
 EXPORTS = ("ra_fwd_rank", "ra_fwd_all", "ra_fwd_rank_ws", "ra_fwd_all_ws", "ra_fwd_workspace_bytes",
+           "ra_fwd_rank_noalloc",
            "ra_ring_step", "ra_ring_step_ws", "ra_kv_append_rr", "ra_attn_partial_rr", "ra_head_a2a",
            "ra_merge_partials", "ra_attn_partial",
            "ra_layout_gather", "ra_last_error", "ra_version")
@@ -59,6 +60,8 @@ def lib() -> ctypes.CDLL:
         L.ra_fwd_all_ws.argtypes = [vp, vp, vp, vp, fp, i32, i32, i32, i64, i32, i32, i32, i32,
                                     i32, i32, i32, vp, i64, vp]
         L.ra_fwd_workspace_bytes.argtypes = [i32, i32, i32, i64, i32, i32, i32, i32, i32, i32, i32]
+        L.ra_fwd_rank_noalloc.argtypes = [vp, vp, vp, vp, fp, i32, i32, i32, i64, i32, i32, i32, i32,
+                                          i32, i32, i32, i32, vp]
         L.ra_ring_step.argtypes = [vp, vp, vp, fp, fp, i32, i32, i32, i64, i32, i32, i32, i32, i32,
                                    i32, i32, vp]
         L.ra_ring_step_ws.argtypes = [vp, vp, vp, fp, fp, i32, i32, i32, i64, i32, i32, i32, i32, i32,
@@ -71,7 +74,8 @@ def lib() -> ctypes.CDLL:
         L.ra_merge_partials.argtypes = [fp, fp, vp, fp, i32, i64, i32, i32, vp]
         L.ra_attn_partial.argtypes = [vp, vp, vp, fp, fp, i32, i32, i32, i64, i64, i32, i32, i32, vp]
         L.ra_layout_gather.argtypes = [vp, vp, i64, i64, i64, i32, i32, i32, vp]
-        for f in ("ra_fwd_rank", "ra_fwd_all", "ra_fwd_rank_ws", "ra_fwd_all_ws", "ra_ring_step", "ra_ring_step_ws",
+        for f in ("ra_fwd_rank", "ra_fwd_all", "ra_fwd_rank_ws", "ra_fwd_all_ws", "ra_fwd_rank_noalloc",
+                  "ra_ring_step", "ra_ring_step_ws",
                   "ra_kv_append_rr", "ra_attn_partial_rr", "ra_head_a2a",
                   "ra_merge_partials", "ra_attn_partial", "ra_layout_gather"):
             getattr(L, f).restype = ctypes.c_int
@@ -201,6 +205,29 @@ def ra_fwd_rank_ws(Q_r, K, V, O_r, LSE_r, P: int, rank: int, causal: bool, layou
                                 _dev(LSE_r, "LSE_r"), B, Hq, Hkv, S, d, P, rank, int(bool(causal)),
                                 _layout(layout), dt, _dtype_code(O_r), int(kv_splits), wp, wb,
                                 _stream(stream)))
+
+
+SCRATCH_BYTES = 64 << 20  # RA_SCRATCH_BYTES: the library's scratch per GPU (ra_fwd_rank_noalloc)
+
+
+def ra_fwd_rank_noalloc(Q_r, K, V, O_r, LSE_r, P: int, rank: int, causal: bool, layout,
+                        kv_splits: int = 0, stream=None):
+    """ra_fwd_rank_ws whose key-range partials go to the library's own device
+    scratch (SCRATCH_BYTES per GPU): the call allocates nothing.  Calls that
+    overlap in time on one GPU share that scratch and must be ordered."""
+    B, S, Hkv, d = K.shape
+    Hq = Q_r.shape[2]
+    if tuple(Q_r.shape) != (B, S // P, Hq, d) or O_r.shape != Q_r.shape or V.shape != K.shape:
+        raise ValueError("shape mismatch")
+    if tuple(LSE_r.shape) != (B, Hq, S // P) or LSE_r.dtype != _torch().float32:
+        raise ValueError("LSE_r must be float32 [B, Hq, S/P]")
+    dt = _dtype_code(Q_r)
+    if not (K.dtype == V.dtype == Q_r.dtype):
+        raise TypeError("Q, K, V must share a dtype")
+    _check(lib().ra_fwd_rank_noalloc(_dev(Q_r, "Q_r"), _dev(K, "K"), _dev(V, "V"), _dev(O_r, "O_r"),
+                                     _dev(LSE_r, "LSE_r"), B, Hq, Hkv, S, d, P, rank,
+                                     int(bool(causal)), _layout(layout), dt, _dtype_code(O_r),
+                                     int(kv_splits), _stream(stream)))
 
 
 def ra_fwd_all_ws(Q, K, V, O, LSE, P: int, causal: bool, layout, kv_splits: int = 0,

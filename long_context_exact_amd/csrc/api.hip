@@ -5,6 +5,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "../../include/ra.h"
 #include "ra_device.h"
 
@@ -225,6 +227,40 @@ int fwd_split(ra::FwdParams p, int d, int dtype, int o_dtype, int kv_splits, voi
     return hip_status(ra::launch_merge(m, d, (hipStream_t)stream), "merge kernel launch");
 }
 
+// ---- library-owned scratch (ra_fwd_rank_noalloc) ---------------------------
+//
+// Device memory for the key-range partials of ra_fwd_rank_noalloc, for callers
+// that cannot allocate.  Each GPU the library runs on holds its own copy of
+// the array until the process ends.  In host code the array's name is only a
+// stand-in for the symbol: kernels and copies use the address that
+// hipGetSymbolAddress returns for the current device, looked up once per
+// device and kept in scratch_dev.
+static __device__ __align__(256) unsigned char scratch[RA_SCRATCH_BYTES];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex scratch_mu;
+void* scratch_dev[kMaxScratchDevices] = {};
+
+// Address of the current device's scratch (set up on the first call there).
+int scratch_ptr(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxScratchDevices)
+        return fail(RA_ERR_UNSUPPORTED, "device %d: scratch is kept for devices 0..%d", dev,
+                    kMaxScratchDevices - 1);
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (scratch_dev[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+        if (p == nullptr) return fail(RA_ERR_HIP, "hipGetSymbolAddress(scratch) returned no address");
+        scratch_dev[dev] = p;
+    }
+    *out = scratch_dev[dev];
+    return RA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -260,6 +296,27 @@ int ra_fwd_rank_ws(const void* Q_r, const void* K, const void* V, void* O_r, flo
     ra::FwdParams p = plan_fwd(Q_r, K, V, O_r, LSE_r, B, Hq, Hkv, S, d, P, causal, layout, dtype,
                                o_dtype, rank, 1, 1);
     return fwd_split(p, d, dtype, o_dtype, kv_splits, workspace, workspace_bytes, stream);
+}
+
+int ra_fwd_rank_noalloc(const void* Q_r, const void* K, const void* V, void* O_r, float* LSE_r, int B,
+                        int Hq, int Hkv, int64_t S, int d, int P, int rank, int causal, int layout,
+                        int dtype, int o_dtype, int kv_splits, void* stream) {
+    int rc = check_fwd(Q_r, K, V, O_r, LSE_r, B, Hq, Hkv, S, d, P, causal, layout, dtype, o_dtype);
+    if (rc != RA_OK) return rc;
+    if (rank < 0 || rank >= P) return fail(RA_ERR_INVALID_ARG, "rank %d outside [0, %d)", rank, P);
+    if (kv_splits < 0 || kv_splits > RA_MAX_KV_SPLITS)
+        return fail(RA_ERR_INVALID_ARG, "kv_splits=%d outside [0, %d]", kv_splits, RA_MAX_KV_SPLITS);
+    ra::FwdParams p = plan_fwd(Q_r, K, V, O_r, LSE_r, B, Hq, Hkv, S, d, P, causal, layout, dtype,
+                               o_dtype, rank, 1, 1);
+    const int64_t need = split_bytes(p, d, kv_splits);
+    if (kv_splits > 1 && need > RA_SCRATCH_BYTES)
+        return fail(RA_ERR_INVALID_ARG,
+                    "kv_splits=%d needs %lld bytes of partials; the library's scratch holds %lld",
+                    kv_splits, (long long)need, (long long)RA_SCRATCH_BYTES);
+    void* ws = nullptr;
+    rc = scratch_ptr(&ws);
+    if (rc != RA_OK) return rc;
+    return fwd_split(p, d, dtype, o_dtype, kv_splits, ws, RA_SCRATCH_BYTES, stream);
 }
 
 int ra_fwd_all_ws(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int Hq,

@@ -159,6 +159,29 @@ def test_fwd_ws_rejects_before_the_device():
                            NULL) == ra.RA_ERR_UNSUPPORTED
 
 
+def test_fwd_noalloc_rejects_before_the_device():
+    L = ra.lib()
+
+    def call(kv_splits, rank=0, **kw):
+        a = dict(B=1, Hq=32, Hkv=8, S=131072, d=128, P=8, causal=1, layout=1, dtype=1, o_dtype=0)
+        a.update(kw)
+        return L.ra_fwd_rank_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, a["B"], a["Hq"], a["Hkv"], a["S"],
+                                     a["d"], a["P"], rank, a["causal"], a["layout"], a["dtype"],
+                                     a["o_dtype"], kv_splits, NULL)
+
+    assert call(-1) == ra.RA_ERR_INVALID_ARG
+    assert call(65) == ra.RA_ERR_INVALID_ARG
+    # two ranges of a 16384-query, 32-head rank share need 541 MB of partials
+    need = ra.ra_fwd_workspace_bytes(1, 32, 8, 131072, 128, 8, False, True, "zigzag", 1, 2)
+    assert need > ra.SCRATCH_BYTES
+    assert call(2) == ra.RA_ERR_INVALID_ARG
+    assert "scratch" in ra.last_error()
+    assert call(0, rank=8) == ra.RA_ERR_INVALID_ARG
+    assert call(0, d=96) == ra.RA_ERR_UNSUPPORTED
+    assert L.ra_fwd_rank_noalloc(NULL, FAKE, FAKE, FAKE, FAKE, 1, 8, 8, 8192, 128, 8, 0, 1, 1, 1, 0, 0,
+                                 NULL) == ra.RA_ERR_INVALID_ARG
+
+
 def test_fwd_workspace_bytes():
     # kv_splits * rows * (d + 1) * 4 with rows = B * Hq * (S/P for a rank, S for all ranks)
     f = ra.ra_fwd_workspace_bytes
@@ -278,6 +301,9 @@ def test_valid_call_without_a_device_reports_hip_error():
     assert rc == ra.RA_ERR_HIP
     assert "launch" in ra.last_error()
     assert L.ra_merge_partials(FAKE, FAKE, FAKE, NULL, 2, 10, 128, 1, NULL) == ra.RA_ERR_HIP
+    # the scratch lookup is the first HIP call of the allocation-free entry point
+    assert L.ra_fwd_rank_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 8, 8192, 128, 8, 0, 1, 1, 1, 0, 0,
+                                 NULL) == ra.RA_ERR_HIP
 
 
 def test_header_is_plain_c(tmp_path):
