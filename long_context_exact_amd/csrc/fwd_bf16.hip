@@ -527,12 +527,10 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdParams p) {
                     else
                         oacc[q % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pp[q / DB], oacc[q % DB], 0, 0, 0);
                     if (j >= 1 && j + AHEAD < NMF) ops[j % AHEAD] = read_op(j + AHEAD);
-                    // The loads of tile i+2 (the loader cursor moved there at
-                    // the end of the previous stage): one behind each even
-                    // slot from the second on, so that their scalar work is
-                    // spread over the stage.  Past the last tile they repeat
-                    // the last tile into the buffer of tile i+2, which no later
-                    // stage reads.
+                    // The loads of K of tile i+3 and V of tile i+2 (the
+                    // loader cursor moved at the end of the previous stage):
+                    // one behind each even slot from the second on, so that
+                    // their scalar work is spread over the stage.
                     if (j >= 2 && (j & 1) == 0 && (j - 2) / 2 < T::LOADS)
                         T::template load_one<RAGGED>((j - 2) / 2, kp_l, klen_l, Vg + voff_l, vlen_l, offs, row_bytes,
                                                      ldsK[(SLOT + 3) % NBUF], ldsV[(SLOT + 2) % NBUF], w, lane);
