@@ -619,7 +619,10 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdParams p) {
     const float lr_tot = halves_sum(lr_run);
     float inv = lr_tot > 0.f ? 1.f / lr_tot : 0.f;
     float lse = l_tot > 0.f ? (m_ref + __log2f(l_tot)) * kLn2 : kNegInf;
-    if (qi < qt.rows) {
+    // A work-group with no key tile leaves a running state as it is (the fold
+    // with an empty block is the identity), and as a key range writes only its
+    // lse = -inf: a merge reads no O of a part with weight 0.
+    if (qi < qt.rows && !(n == 0 && p.fold)) {
         const int64_t obase = ((qt.b * p.q_rows + qt.q_row0 + qi) * p.Hq + qt.qh) * (int64_t)D +
                               (int64_t)split * p.o_split_stride;
         const int64_t lidx = ((int64_t)qt.b * p.Hq + qt.qh) * p.q_rows + qt.q_row0 + qi +
@@ -636,8 +639,9 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdParams p) {
                 lse = M + __logf(a + b);
             }
         }
+        const bool o_store = !(n == 0 && p.kv_splits > 1);
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+        for (int db = 0; db < DB && o_store; ++db)
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
                 // accumulator registers 4*g4..4*g4+3 hold dims db*32 + 8*g4 + 4h + 0..3

@@ -50,7 +50,10 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
         const int q = q0 + lane;
         M = fmaxf(M, q < p.n_parts ? p.lse_parts[(int64_t)q * p.rows + lrow] : kNegInf);
     }
-    M = fmaxf(wave_max(M), ls);
+    M = wave_max(M);
+    // no part has a key: a running state stays as it is
+    if (M == kNegInf && p.lse_state != nullptr) return;
+    M = fmaxf(M, ls);
 
     float acc[EPL];
 #pragma unroll
@@ -122,13 +125,16 @@ __global__ __launch_bounds__(256) void merge_few_kernel(MergeParams p) {
         lrow = (b * p.Hq + h) * p.q_rows + q;
     }
     float lq[MERGE_FEW_MAX];
-    const float ls = p.lse_state != nullptr ? p.lse_state[lrow] : kNegInf;
-    float M = ls;
+    float M = kNegInf;
 #pragma unroll
     for (int q = 0; q < MERGE_FEW_MAX; ++q) {
         lq[q] = q < p.n_parts ? p.lse_parts[(int64_t)q * p.rows + lrow] : kNegInf;
         M = fmaxf(M, lq[q]);
     }
+    // no part has a key: a running state stays as it is
+    if (M == kNegInf && p.lse_state != nullptr) return;
+    const float ls = p.lse_state != nullptr ? p.lse_state[lrow] : kNegInf;
+    M = fmaxf(M, ls);
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     float W = 0.f;
     if (M != kNegInf) {
