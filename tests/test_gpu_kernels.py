@@ -491,6 +491,46 @@ def test_ring_step_automatic_and_many_ranges():
     log(f"  12 ranges ok {fmt(e)}")
 
 
+def test_ring_step_without_visible_keys_keeps_the_state():
+    """A step whose block holds no key visible to some query rows leaves those
+    rows of the running state exactly as they were (the fold with an empty
+    block is the identity), with one key range and with several; the rows
+    that do see keys reach the oracle.  Zig-zag, P = 4: rank 0 holds chunks 0
+    and 7, and after step 0 no later block has a key for chunk 0."""
+    B, S, Hq, Hkv, d, P, layout, causal = 1, 4096, 4, 2, 128, 4, "zigzag", True
+    log("ring steps with fully masked tiles")
+    Qn, Kn, Vn = qkv(B, S, S, Hq, Hkv, d, "bf16", (1380, S, P))
+    Qs, Ks, Vs = (to_dev(shard(x, S, P, layout)) for x in (Qn, Kn, Vn))
+    O_ref, lse_ref = oracle.attention(Qn, Kn, Vn, causal)
+    n, c, r = S // P, S // (2 * P), 0
+    Qr = Qs[:, :n].contiguous()
+    for splits in (None, 3):
+        O = torch.empty(B, n, Hq, d, dtype=torch.float32, device="cuda")
+        L = torch.empty(B, Hq, n, dtype=torch.float32, device="cuda")
+        ws = None
+        if splits is not None:
+            nb = ra.ra_fwd_workspace_bytes(B, Hq, Hkv, S, d, P, False, causal, layout, ra.DTYPE_BF16, splits)
+            ws = torch.full((nb // 4,), float("nan"), dtype=torch.float32, device="cuda")
+        early = None
+        for t in range(P):
+            s = (r - t) % P
+            Kb, Vb = Ks[:, s * n:(s + 1) * n].contiguous(), Vs[:, s * n:(s + 1) * n].contiguous()
+            if splits is None:
+                ra.ra_ring_step(Qr, Kb, Vb, O, L, S, P, r, t, causal, layout)
+            else:
+                ra.ra_ring_step_ws(Qr, Kb, Vb, O, L, S, P, r, t, causal, layout, splits, ws)
+            torch.cuda.synchronize()
+            if t == 0:
+                early = (O[:, :c].clone(), L[:, :, :c].clone())
+            else:
+                assert torch.equal(O[:, :c], early[0]) and torch.equal(L[:, :, :c], early[1]), \
+                    f"splits {splits}: step {t} changed the rows of chunk 0"
+        # rank 0's rows: chunk 0 (positions 0..c-1) and chunk 7 (the last c)
+        pos = np.concatenate([np.arange(c), np.arange(S - c, S)])
+        e = check(from_dev(O), O_ref[:, pos], from_dev(L), lse_ref[:, :, pos], "bf16", f"splits {splits}")
+        log(f"  splits={splits} ok {fmt(e)}")
+
+
 def test_ring_step_double_buffered_streams():
     """The schedule a multi-GPU ring would run: while step t computes on one
     receive buffer, the next block is copied into the other on a second
