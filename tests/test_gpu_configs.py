@@ -1,5 +1,6 @@
 """GPU parity at the five workload sizes of the hot path, in the launch
-configuration the benchmark times.
+configurations the benchmark times (for the prefill: the plain entry points
+and the _ws ones with the automatic key-range count).
 
 Small workloads are checked on every output row; the 32k and 128k-token
 workloads on seeded sampled rows (per rank: the first and last row of each
@@ -75,20 +76,65 @@ def test_prefill_workload(cfg, layout):
         assert torch.equal(_bits(Ob), _bits(O.to(torch.bfloat16))) and torch.equal(Lb, L)
         del Ob, Lb
 
-    O_h = unshard(from_dev(O), S, P, lay, axis=1)
-    L_h = unshard(from_dev(L), S, P, lay, axis=2)
+    # The benchmark times the _ws entry points with the automatic key-range
+    # count: each rank's share (ra_fwd_rank_ws) and all ranks in one launch
+    # (ra_fwd_all_ws).  Where the count is one they are the launches above, bit
+    # for bit; otherwise their results go to the oracle as well.
+    outs = [("ra_fwd_all", O, L)]
+    code = ra.DTYPE_BF16 if w.dtype == "bf16" else ra.DTYPE_F32
+    nb_r = ra.ra_fwd_workspace_bytes(w.B, w.Hq, w.Hkv, S, w.d, P, False, w.causal, lay, code, 0)
+    nb_a = ra.ra_fwd_workspace_bytes(w.B, w.Hq, w.Hkv, S, w.d, P, True, w.causal, lay, code, 0)
+    ws_r = torch.full((max(nb_r, 16) // 4,), float("nan"), dtype=torch.float32, device="cuda")
+    O_r = torch.empty_like(O)
+    L_r = torch.empty_like(L)
+    for r in ranks:
+        log(f"workload {cfg}: ra_fwd_rank_ws({r}), automatic ranges")
+        Qr = Qs[:, r * n:(r + 1) * n]
+        Orw = torch.empty(Qr.shape, dtype=torch.float32, device="cuda")
+        Lrw = torch.empty(w.B, w.Hq, n, dtype=torch.float32, device="cuda")
+        ra.ra_fwd_rank_ws(Qr, Ks, Vs, Orw, Lrw, P, r, w.causal, lay, 0, ws_r if nb_r else None)
+        torch.cuda.synchronize()
+        O_r[:, r * n:(r + 1) * n] = Orw
+        L_r[:, :, r * n:(r + 1) * n] = Lrw
+        if nb_r == 0:
+            assert torch.equal(Orw, O[:, r * n:(r + 1) * n]) and torch.equal(Lrw, L[:, :, r * n:(r + 1) * n])
+        del Orw, Lrw
+    del ws_r
+    if nb_r and len(ranks) == P:
+        outs.append(("ra_fwd_rank_ws", O_r, L_r))
+    else:
+        del O_r, L_r
+    log(f"workload {cfg}: ra_fwd_all_ws, automatic ranges")
+    ws_a = torch.full((max(nb_a, 16) // 4,), float("nan"), dtype=torch.float32, device="cuda")
+    O_a = torch.empty_like(O)
+    L_a = torch.empty_like(L)
+    ra.ra_fwd_all_ws(Qs, Ks, Vs, O_a, L_a, P, w.causal, lay, 0, ws_a if nb_a else None)
+    torch.cuda.synchronize()
+    del ws_a
+    if nb_a == 0:
+        assert torch.equal(O_a, O) and torch.equal(L_a, L)
+        del O_a, L_a
+    else:
+        outs.append(("ra_fwd_all_ws", O_a, L_a))
     del Qs, Ks, Vs, O, L
+    hosts = []
+    for what, Od, Ld in outs:
+        hosts.append((what, unshard(from_dev(Od), S, P, lay, axis=1), unshard(from_dev(Ld), S, P, lay, axis=2)))
+    del outs, Od, Ld
     torch.cuda.empty_cache()
     if cfg <= 2:
         log(f"workload {cfg}: oracle on all {S} rows")
         O_ref, L_ref = oracle.attention(Qn, Kn, Vn, w.causal)
-        e = check(O_h, O_ref, L_h, L_ref, w.dtype, w.name)
+        for what, O_h, L_h in hosts:
+            e = check(O_h, O_ref, L_h, L_ref, w.dtype, f"{w.name} {what}")
+            log(f"workload {cfg} {what}: ok {fmt(e)}")
     else:
         rows = sample_rows(S, P, lay, ROWS_PER_RANK, [cfg, 3])
         log(f"workload {cfg}: oracle on {len(rows)} sampled rows")
         O_ref, L_ref = oracle.attention_rows(Qn, Kn, Vn, w.causal, np.zeros_like(rows), rows)
-        e = check(O_h[0, rows], O_ref, L_h[0][:, rows].T, L_ref, w.dtype, w.name)
-    log(f"workload {cfg}: ok {fmt(e)}")
+        for what, O_h, L_h in hosts:
+            e = check(O_h[0, rows], O_ref, L_h[0][:, rows].T, L_ref, w.dtype, f"{w.name} {what}")
+            log(f"workload {cfg} {what}: ok {fmt(e)}")
 
 
 def _check_decode_sequences(w, qh, O_g, L_g, what):
