@@ -231,3 +231,52 @@ def test_decode_workload_round_robin_cache():
     del Kc, Vc, Op, lp
     torch.cuda.empty_cache()
     _check_decode_sequences(w, qh, O_g, L_g, "round-robin cache")
+
+
+@pytest.mark.parametrize("cfg", [3, 4])
+def test_ring_steps_workload(cfg):
+    """The ring-step launches the benchmark times (``--ring-steps``): rank 0's
+    P steps of the 32k and 128k-token workloads, each on a copy of the block
+    that has arrived, with one key range (ra_ring_step) and with the automatic
+    count (ra_ring_step_ws).  Both against the oracle on rank 0's sampled
+    rows (the first and last row of each of its chunks plus 60 drawn with
+    numpy.random.default_rng([cfg, 4, 0])), every query head."""
+    w = WORKLOADS[cfg]
+    log(f"workload {cfg} {w.name}: ring steps, generating inputs")
+    Qn, Kn, Vn = _inputs(w)
+    S, P, lay = w.S, w.P, w.layout
+    Qs, Ks, Vs = (to_dev(shard(x, S, P, lay)) for x in (Qn, Kn, Vn))
+    n, r = S // P, 0
+    Qr = Qs[:, :n].contiguous()
+    code = ra.DTYPE_BF16 if w.dtype == "bf16" else ra.DTYPE_F32
+    nb = ra.ra_fwd_workspace_bytes(w.B, w.Hq, w.Hkv, S, w.d, P, False, w.causal, lay, code, 0)
+    ws = torch.full((max(nb, 16) // 4,), float("nan"), dtype=torch.float32, device="cuda")
+    outs = []
+    for splits in (None, 0):
+        O = torch.empty(w.B, n, w.Hq, w.d, dtype=torch.float32, device="cuda")
+        L = torch.empty(w.B, w.Hq, n, dtype=torch.float32, device="cuda")
+        for t in range(P):
+            s = (r - t) % P
+            Kb = Ks[:, s * n:(s + 1) * n].contiguous()
+            Vb = Vs[:, s * n:(s + 1) * n].contiguous()
+            if splits is None:
+                ra.ra_ring_step(Qr, Kb, Vb, O, L, S, P, r, t, w.causal, lay)
+            else:
+                ra.ra_ring_step_ws(Qr, Kb, Vb, O, L, S, P, r, t, w.causal, lay, splits, ws)
+            del Kb, Vb
+        torch.cuda.synchronize()
+        outs.append(("ra_ring_step" if splits is None else "ra_ring_step_ws", from_dev(O), from_dev(L)))
+        del O, L
+    del Qs, Ks, Vs, Qr, ws
+    torch.cuda.empty_cache()
+    # rank 0's local rows: the two ends of each chunk and 60 drawn rows
+    pos = oracle.natural_positions(S, P, lay)[:n]
+    c = oracle.chunk_len(lay, S, P)
+    local = [k for k0 in range(0, n, c) for k in (k0, k0 + c - 1)]
+    local += list(np.random.default_rng([cfg, 4, 0]).choice(n, size=ROWS_PER_RANK, replace=False))
+    local = np.unique(np.asarray(local, dtype=np.int64))
+    log(f"workload {cfg}: oracle on {len(local)} rows of rank 0")
+    O_ref, L_ref = oracle.attention_rows(Qn, Kn, Vn, w.causal, np.zeros_like(local), pos[local])
+    for what, O_h, L_h in outs:
+        e = check(O_h[0, local], O_ref, L_h[0][:, local].T, L_ref, w.dtype, f"{w.name} {what}")
+        log(f"workload {cfg} {what}: ok {fmt(e)}")
