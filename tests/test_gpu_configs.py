@@ -47,6 +47,16 @@ def test_prefill_workload(cfg, layout):
     Qn, Kn, Vn = _inputs(w)
     S, P, lay = w.S, w.P, w.layout
     Qs, Ks, Vs = (to_dev(shard(x, S, P, lay)) for x in (Qn, Kn, Vn))
+    # the benchmark's first stage: the layout kernel gathers the natural-order
+    # tensors on the device into the sharded order, equal to the host's
+    for name, x, xs in (("Q", Qn, Qs), ("K", Kn, Ks), ("V", Vn, Vs)):
+        xn = to_dev(x)
+        xg = torch.empty_like(xn)
+        ra.ra_layout_gather(xn, xg, S, P, lay, inverse=False)
+        torch.cuda.synchronize()
+        raw = torch.int16 if xg.dtype == torch.bfloat16 else torch.int32
+        assert torch.equal(xg.view(raw), xs.view(raw)), f"layout gather of {name}"
+        del xn, xg
     # fp32 output: the accumulator unrounded (a bf16 output is the same values
     # rounded to nearest even, checked below)
     O = torch.empty(w.B, S, w.Hq, w.d, dtype=torch.float32, device="cuda")
