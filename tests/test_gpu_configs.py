@@ -290,3 +290,51 @@ def test_ring_steps_workload(cfg):
     for what, O_h, L_h in outs:
         e = check(O_h[0, local], O_ref, L_h[0][:, local].T, L_ref, w.dtype, f"{w.name} {what}")
         log(f"workload {cfg} {what}: ok {fmt(e)}")
+
+
+@pytest.mark.parametrize("cfg", [3, 4])
+def test_ulysses_workload(cfg):
+    """The Ulysses launches the benchmark times (``--ulysses``) on the 32k and
+    128k-token workloads: all-to-all of Q, K, V from natural order to P head
+    groups (ra_head_a2a), attention of the groups as one batch over the whole
+    sequence (ra_fwd_all_ws, one shard, automatic key ranges), all-to-all of
+    O and LSE back; against the oracle on the sampled rows of
+    test_prefill_workload, every query head."""
+    w = WORKLOADS[cfg]
+    log(f"workload {cfg} {w.name}: Ulysses, generating inputs")
+    Qn, Kn, Vn = _inputs(w)
+    B, S, P, d = w.B, w.S, w.P, w.d
+    Gq, Gkv = w.Hq // P, w.Hkv // P
+    Qd, Kd, Vd = to_dev(Qn), to_dev(Kn), to_dev(Vn)
+    Qh = torch.empty(P * B, S, Gq, d, dtype=Qd.dtype, device="cuda")
+    Kh = torch.empty(P * B, S, Gkv, d, dtype=Kd.dtype, device="cuda")
+    Vh = torch.empty_like(Kh)
+    es = Qd.element_size()
+    ra.ra_head_a2a(Qd, Qh, B, S, P, Gq * d * es, False)
+    ra.ra_head_a2a(Kd, Kh, B, S, P, Gkv * d * es, False)
+    ra.ra_head_a2a(Vd, Vh, B, S, P, Gkv * d * es, False)
+    del Qd, Kd, Vd
+    Oh = torch.empty(P * B, S, Gq, d, dtype=torch.float32, device="cuda")
+    Lh = torch.empty(P * B, Gq, S, dtype=torch.float32, device="cuda")
+    code = ra.DTYPE_BF16 if w.dtype == "bf16" else ra.DTYPE_F32
+    nb = ra.ra_fwd_workspace_bytes(P * B, Gq, Gkv, S, d, 1, True, w.causal, "contiguous", code, 0)
+    ws = torch.full((max(nb, 16) // 4,), float("nan"), dtype=torch.float32, device="cuda")
+    log(f"workload {cfg}: ra_fwd_all_ws over {P} head groups, {nb} workspace bytes")
+    ra.ra_fwd_all_ws(Qh, Kh, Vh, Oh, Lh, 1, w.causal, "contiguous", 0, ws if nb else None)
+    del Qh, Kh, Vh, ws
+    O = torch.empty(B, S, w.Hq, d, dtype=torch.float32, device="cuda")
+    L = torch.empty(B, w.Hq, S, dtype=torch.float32, device="cuda")
+    ra.ra_head_a2a(Oh, O, B, S, P, Gq * d * 4, True)
+    ra.ra_head_a2a(Lh, L, B, 1, P, Gq * S * 4, True)
+    torch.cuda.synchronize()
+    del Oh, Lh
+    rows = sample_rows(S, P, w.layout, ROWS_PER_RANK, [cfg, 3])
+    idx = torch.as_tensor(rows, device="cuda")
+    O_h = from_dev(O[0, idx])
+    L_h = from_dev(L[0][:, idx]).T
+    del O, L
+    torch.cuda.empty_cache()
+    log(f"workload {cfg}: oracle on {len(rows)} sampled rows")
+    O_ref, L_ref = oracle.attention_rows(Qn, Kn, Vn, w.causal, np.zeros_like(rows), rows)
+    e = check(O_h, O_ref, L_h, L_ref, w.dtype, f"{w.name} Ulysses")
+    log(f"workload {cfg} Ulysses: ok {fmt(e)}")
