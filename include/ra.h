@@ -182,7 +182,7 @@ int ra_fwd_all_ws(const void* Q, const void* K, const void* V, void* O, float* L
  * scratch's contents on entry do not matter; every range rewrites its
  * partials.  All other arguments and requirements are those of ra_fwd_rank.
  */
-#define RA_SCRATCH_BYTES ((int64_t)64 << 20)
+#define RA_SCRATCH_BYTES ((int64_t)128 << 20)
 
 int ra_fwd_rank_noalloc(const void* Q_r, const void* K, const void* V, void* O_r, float* LSE_r,
                         int B, int Hq, int Hkv, int64_t S, int d, int P, int rank,

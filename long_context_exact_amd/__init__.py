@@ -207,7 +207,7 @@ def ra_fwd_rank_ws(Q_r, K, V, O_r, LSE_r, P: int, rank: int, causal: bool, layou
                                 _stream(stream)))
 
 
-SCRATCH_BYTES = 64 << 20  # RA_SCRATCH_BYTES: the library's scratch per GPU (ra_fwd_rank_noalloc)
+SCRATCH_BYTES = 128 << 20  # RA_SCRATCH_BYTES: the library's scratch per GPU (ra_fwd_rank_noalloc)
 
 
 def ra_fwd_rank_noalloc(Q_r, K, V, O_r, LSE_r, P: int, rank: int, causal: bool, layout,

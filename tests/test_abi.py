@@ -174,6 +174,9 @@ def test_fwd_noalloc_rejects_before_the_device():
     # two ranges of a 16384-query, 32-head rank share need 541 MB of partials
     need = ra.ra_fwd_workspace_bytes(1, 32, 8, 131072, 128, 8, False, True, "zigzag", 1, 2)
     assert need > ra.SCRATCH_BYTES
+    # the automatic ranges of the 32k and 8k-token rank shares fit
+    assert 0 < ra.ra_fwd_workspace_bytes(1, 16, 16, 32768, 128, 8, False, True, "zigzag", 1, 0) <= ra.SCRATCH_BYTES
+    assert 0 < ra.ra_fwd_workspace_bytes(1, 8, 8, 8192, 128, 8, False, True, "contiguous", 1, 0) <= ra.SCRATCH_BYTES
     assert call(2) == ra.RA_ERR_INVALID_ARG
     assert "scratch" in ra.last_error()
     assert call(0, rank=8) == ra.RA_ERR_INVALID_ARG
