@@ -208,7 +208,9 @@ int fwd_split(ra::FwdParams p, int d, int dtype, int o_dtype, int kv_splits, voi
     p.kv_splits = splits;
     p.o_split_stride = rows * d;
     p.l_split_stride = rows;
-    p.xcd_pairs = 0;  // keep the splits of one tile adjacent in dispatch order
+    // the bf16 kernel keeps a tile's ranges on the tile's XCD; the fp32 one
+    // keeps them adjacent in dispatch order, without XCD grouping
+    if (dtype != RA_DTYPE_BF16) p.xcd_pairs = 0;
     const int rc = launch_fwd(p, d, dtype, stream);
     if (rc != RA_OK) return rc;
     ra::MergeParams m;

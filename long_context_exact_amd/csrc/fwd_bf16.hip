@@ -329,8 +329,19 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdParams p) {
     __shared__ __attribute__((aligned(1024))) uint16_t ldsV[NBUF][T::ELEMS];
 
     // work-group -> (query tile, key range): the splits of one tile are adjacent
-    const unsigned split = blockIdx.x % (unsigned)p.kv_splits;
-    const QTile qt = decode_qtile<BM>(p, blockIdx.x / (unsigned)p.kv_splits);
+    // With XCD grouping the ranges of one tile stay on the tile's XCD
+    // (work-group ids 8 apart, as dispatch deals ids round-robin over the 8
+    // XCDs), next to each other in its dispatch order.
+    unsigned split, qid;
+    if (p.xcd_pairs > 0 && p.kv_splits > 1) {
+        const unsigned k = blockIdx.x >> 3;
+        split = k % (unsigned)p.kv_splits;
+        qid = ((k / (unsigned)p.kv_splits) << 3) | (blockIdx.x & 7u);
+    } else {
+        split = blockIdx.x % (unsigned)p.kv_splits;
+        qid = blockIdx.x / (unsigned)p.kv_splits;
+    }
+    const QTile qt = decode_qtile<BM>(p, qid);
     const int t = threadIdx.x;
     const int lane = t & 63;
     const int w = __builtin_amdgcn_readfirstlane(t >> 6);  // wave index, uniform in the wave
